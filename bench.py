@@ -1,0 +1,226 @@
+"""Throughput of the MoE FFN-service layer on one MI355X.
+
+One step = one forward of the whole layer (router + top-k, dispatch,
+[quantise], gate/up GEMM + SwiGLU, down GEMM, shared expert, combine) over
+one batch of seeded synthetic hidden states already resident in HBM.
+
+Default workload: decode micro-batch T=256, h=4096, E=64 routed experts,
+top-8, SwiGLU intermediate 1536, one shared expert (1536), bf16 with fp32
+accumulation.  Prints one JSON line.  Extra fields: "roofline" of the
+dominant kernel (gate/up GEMM, timed with HIP events on the forward's stream
+over the timed region) and "cpu_baseline" (the fp64 oracle on the host).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-FFN layer tokens/s on 1 MI355X + % of HBM-BW / MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "w8a8": 5000.0, "f32": 157.3}
+DEFAULT_WORKLOAD = "decode_h4096_e64"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "expert_side_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def work_model(s, counts):
+    """Algorithmic bytes and flops of one forward, from the per-expert counts.
+
+    Bytes: weights of the experts that received rows (+ E4M3 block scales),
+    the router, the shared experts, the input and the output.  Intermediates
+    (Z, Y) are the implementation's own traffic and are not counted."""
+    wb = 1 if s.mode == "w8a8" else (4 if s.mode == "f32" else 2)
+    ab = 4 if s.mode == "f32" else 2
+    touched = int(sum(1 for c in counts if c > 0))
+    scale_b = (4 / (128 * 128)) if s.mode == "w8a8" else 0.0
+    per_gu = 2 * s.I * s.h * (wb + scale_b)
+    per_dn = s.h * s.I * (wb + scale_b)
+    sh_gu = s.S * 2 * s.Is * s.h * (wb + scale_b)
+    sh_dn = s.S * s.h * s.Is * (wb + scale_b)
+    io = 2 * s.T * s.h * ab
+    router = s.E * s.h * ab
+    gate_up_bytes = touched * per_gu + sh_gu + s.T * s.h * ab
+    flops = (2 * s.T * s.k * 3 * s.h * s.I + 2 * s.T * s.S * 3 * s.h * s.Is
+             + 2 * s.T * s.h * s.E)
+    gate_up_flops = 2 * s.T * s.k * 2 * s.h * s.I + 2 * s.T * s.S * 2 * s.h * s.Is
+    return {
+        "touched_experts": touched,
+        "gate_up_bytes": gate_up_bytes,
+        "gate_up_flops": gate_up_flops,
+        "forward_bytes": touched * (per_gu + per_dn) + sh_gu + sh_dn + io + router,
+        "forward_flops": flops,
+        "per_expert_gate_up_bytes": per_gu,
+    }
+
+
+def cpu_baseline(syn, min_seconds=10.0):
+    """The fp64 oracle on the same batch, weights pre-drawn in host memory."""
+    import numpy as np
+    from oracle import afd_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    s = syn.shape
+    g, u, d = syn.stacked_experts()
+    sh = syn.stacked_shared()
+    wr, b = syn.router_weight(), syn.router_bias()
+
+    class Src:
+        shape = s
+
+        def router_weight(self):
+            return wr
+
+        def router_bias(self):
+            return b
+
+        def expert(self, e):
+            return g[e], u[e], d[e]
+
+        def shared(self, j):
+            return sh[0][j], sh[1][j], sh[2][j]
+
+    orc = O.OracleFFN(Src())
+    x = syn.hidden()
+    tokens, t0 = 0, time.perf_counter()
+    while True:
+        orc.forward(x)
+        tokens += s.T
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {"value": tokens / el, "unit": "tokens/s", "cores": int(min(cores, blas_threads)),
+            "kind": "oracle",
+            "sample": f"full {s.name} batch of {s.T} tokens, {tokens // s.T} pass(es), "
+                      f"{el:.1f} s; fp64 NumPy/OpenBLAS, weights pre-drawn in host RAM; "
+                      f"host has {cores} cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the layer runs on a single MI355X "
+              f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from afd_inputs import CONFIGS, SyntheticLayer
+    from expert_side_attention_amd.workload import build_layer, hidden_tensor
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    shape = CONFIGS[args.workload]
+    if shape.micro_batches != 1:
+        raise SystemExit("two-stream workloads are timed by their own script")
+    syn = SyntheticLayer(shape, seed=args.seed)
+    dev = "cuda:0"
+    log(f"[bench] building {shape.name} on {dev}")
+    layer = build_layer(syn, dev)
+    x = hidden_tensor(syn, dev)
+    out = torch.empty_like(x)
+    _, tr = layer.forward(x, trace=True)
+    torch.cuda.synchronize()
+    counts = tr["counts"].cpu().tolist()
+    model = work_model(shape, counts)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        layer.forward(x, out=out, stream=stream)
+    torch.cuda.synchronize()
+    layer.profile_read()  # reset
+
+    # timed region: K steps; HIP events around the gate/up GEMM launches
+    layer.profile_enable(["gate_up"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, out=out, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = layer.profile_read()
+    layer.profile_enable([])
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    gu_ms, gu_n = prof["gate_up"]
+    gu_avg = gu_ms / max(gu_n, 1)
+
+    # untimed breakdown of all stages
+    layer.profile_enable(["router", "dispatch", "quant", "gate_up", "down", "combine"])
+    for _ in range(10):
+        layer.forward(x, out=out, stream=stream)
+    torch.cuda.synchronize()
+    stages = {k: round(v[0] / v[1], 4) for k, v in layer.profile_read().items() if v[1]}
+    layer.profile_enable([])
+
+    achieved = model["gate_up_bytes"] / (gu_avg * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{shape.name}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("hbm_bytes_per_launch")
+    value = shape.T / (ms_step * 1e-3)
+    fwd_gbs = model["forward_bytes"] / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.mode if shape.mode != "w8a8" else "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) hidden states, N(0,0.02) weights; no trained weights)",
+        "config": {"workload": shape.name, "T": shape.T, "h": shape.h, "E": shape.E,
+                   "k": shape.k, "I": shape.I, "S": shape.S, "Is": shape.Is,
+                   "mode": shape.mode, "seed": args.seed},
+        "roofline": {"bound": "hbm", "kernel": "gate_up grouped GEMM + SwiGLU",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(gu_avg, 5),
+                     "algorithmic_bytes_per_launch": int(model["gate_up_bytes"])},
+        "forward": {"hbm_gbs": round(fwd_gbs, 1), "hbm_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
+                    "bytes": int(model["forward_bytes"]),
+                    "tflops": round(model["forward_flops"] / (ms_step * 1e-3) / 1e12, 2),
+                    "touched_experts": model["touched_experts"],
+                    "stage_ms": stages},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(syn)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

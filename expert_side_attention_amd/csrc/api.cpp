@@ -1,0 +1,445 @@
+// C ABI of the MoE FFN-service layer: validation, workspace, and the
+// sequence of kernel launches of one forward (router -> dispatch ->
+// [quantise] -> gate/up -> down -> combine) on the caller's stream.
+//
+// The FFN side of Attention-FFN Disaggregation runs this step on the hidden
+// states it receives and returns the result (vLLM AFD plugin page, "系統架構
+// / 2. FFN Service"); misuse of the FFN side fails at once rather than
+// degrading silently (plugin article, "Ejecutarlo en una sola máquina"),
+// which is the error policy here: every argument is checked before anything
+// is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/afd_ffn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(AFD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct StageEvents {
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct afd_ffn_handle {
+  afd_ffn_config cfg;
+  afd_ffn_weights w;
+  int device;
+  int elem;    // 0 f32, 1 bf16, 2 fp8 (GEMM operand type)
+  int zpitch;  // Z row length in elements: max(I, I_s)
+  int bm;      // row tile height
+  int tiles_cap;
+  void *ws;
+  size_t ws_bytes;
+  int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles;
+  float *topk_w;
+  afd::Tile *tiles;
+  uint8_t *xq;
+  float *xs;
+  uint8_t *z;
+  float *zs;
+  uint8_t *y;
+  // profiling
+  uint32_t prof_mask;
+  std::vector<StageEvents> ev_pool;
+  std::vector<int> ev_stage;
+  size_t ev_used;
+};
+
+namespace {
+
+int64_t tiles_upper_bound(int64_t T, int k, int E, int S, int bm) {
+  const int64_t tk = T * k;
+  const int64_t routed = (tk + bm - 1) / bm + (tk < E ? tk : E);
+  return routed + S * ((T + bm - 1) / bm);
+}
+
+int validate_config(const afd_ffn_config *c) {
+  if (!c) return fail(AFD_ERR_INVALID_ARG, "config is NULL");
+  if (c->abi_version != AFD_FFN_ABI_VERSION)
+    return fail(AFD_ERR_INVALID_ARG, "abi_version %u, library has %u", c->abi_version,
+                AFD_FFN_ABI_VERSION);
+  if (c->mode > AFD_MODE_W8A8_E4M3) return fail(AFD_ERR_INVALID_ARG, "unknown mode %u", c->mode);
+  if (c->num_experts < 1 || c->num_experts > afd::kMaxExperts)
+    return fail(c->num_experts < 1 ? AFD_ERR_INVALID_ARG : AFD_ERR_UNSUPPORTED,
+                "num_experts %d outside [1, %d]", c->num_experts, afd::kMaxExperts);
+  if (c->top_k < 1 || c->top_k > c->num_experts)
+    return fail(AFD_ERR_INVALID_ARG, "top_k %d outside [1, num_experts=%d]", c->top_k,
+                c->num_experts);
+  if (c->hidden < 128 || c->hidden % 128)
+    return fail(AFD_ERR_INVALID_ARG, "hidden %d must be a positive multiple of 128", c->hidden);
+  if (c->inter < 128 || c->inter % 128)
+    return fail(AFD_ERR_INVALID_ARG, "inter %d must be a positive multiple of 128", c->inter);
+  if (c->num_shared < 0 || c->num_shared > afd::kMaxShared)
+    return fail(AFD_ERR_INVALID_ARG, "num_shared %d outside [0, %d]", c->num_shared,
+                afd::kMaxShared);
+  if (c->num_shared > 0 && (c->shared_inter < 128 || c->shared_inter % 128))
+    return fail(AFD_ERR_INVALID_ARG, "shared_inter %d must be a positive multiple of 128",
+                c->shared_inter);
+  if (c->max_tokens < 1 || c->max_tokens > (1 << 20))
+    return fail(AFD_ERR_INVALID_ARG, "max_tokens %d outside [1, 2^20]", c->max_tokens);
+  if (static_cast<int64_t>(c->max_tokens) * (c->top_k + c->num_shared) >= (1LL << 31))
+    return fail(AFD_ERR_INVALID_ARG, "max_tokens * (top_k + num_shared) must be < 2^31");
+  if (c->has_router_bias != 0 && c->has_router_bias != 1)
+    return fail(AFD_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
+  return AFD_OK;
+}
+
+int validate_weights(const afd_ffn_config *c, const afd_ffn_weights *w) {
+  if (!w) return fail(AFD_ERR_INVALID_ARG, "weights is NULL");
+  if (!w->router_w || !w->gate_w || !w->up_w || !w->down_w)
+    return fail(AFD_ERR_INVALID_ARG, "router_w, gate_w, up_w and down_w are required");
+  if (c->has_router_bias && !w->router_b)
+    return fail(AFD_ERR_INVALID_ARG, "has_router_bias = 1 but router_b is NULL");
+  const bool fp8 = c->mode == AFD_MODE_W8A8_E4M3;
+  if (fp8 && (!w->gate_s || !w->up_s || !w->down_s))
+    return fail(AFD_ERR_INVALID_ARG, "W8A8 needs gate_s, up_s and down_s");
+  if (c->num_shared > 0) {
+    if (!w->sh_gate_w || !w->sh_up_w || !w->sh_down_w)
+      return fail(AFD_ERR_INVALID_ARG, "num_shared > 0 needs sh_gate_w, sh_up_w, sh_down_w");
+    if (fp8 && (!w->sh_gate_s || !w->sh_up_s || !w->sh_down_s))
+      return fail(AFD_ERR_INVALID_ARG, "W8A8 with shared experts needs sh_*_s");
+  }
+  return AFD_OK;
+}
+
+// Record a profiling event pair around one stage's launches.
+hipEvent_t *prof_begin(afd_ffn_handle *h, int stage, hipStream_t s) {
+  if (!(h->prof_mask & (1u << stage))) return nullptr;
+  if (h->ev_used == h->ev_pool.size()) {
+    StageEvents e;
+    if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess)
+      return nullptr;
+    h->ev_pool.push_back(e);
+    h->ev_stage.push_back(stage);
+  }
+  StageEvents &e = h->ev_pool[h->ev_used];
+  h->ev_stage[h->ev_used] = stage;
+  ++h->ev_used;
+  hipEventRecord(e.start, s);
+  return &e.stop;
+}
+void prof_end(hipEvent_t *stop, hipStream_t s) {
+  if (stop) hipEventRecord(*stop, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *afd_ffn_last_error(void) { return g_last_error.c_str(); }
+
+int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
+                   afd_ffn_handle **out) {
+  if (!out) return fail(AFD_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  rc = validate_weights(cfg, w);
+  if (rc) return rc;
+
+  afd_ffn_handle *h = new afd_ffn_handle();
+  h->cfg = *cfg;
+  h->w = *w;
+  hipGetDevice(&h->device);
+  h->elem = cfg->mode == AFD_MODE_F32 ? 0 : (cfg->mode == AFD_MODE_BF16 ? 1 : 2);
+  const int S = cfg->num_shared;
+  h->zpitch = (S > 0 && cfg->shared_inter > cfg->inter) ? cfg->shared_inter : cfg->inter;
+  const int64_t T = cfg->max_tokens, k = cfg->top_k, E = cfg->num_experts;
+  const int64_t hd = cfg->hidden;
+  h->bm = afd::gemm_bm(h->elem, cfg->max_tokens, cfg->top_k, cfg->num_experts);
+  h->tiles_cap = static_cast<int>(tiles_upper_bound(T, cfg->top_k, cfg->num_experts, S, 16));
+
+  const int64_t R = T * k + S * T;  // dispatched + shared rows
+  const int zes = h->elem == 0 ? 4 : (h->elem == 1 ? 2 : 1);
+  const int yes = h->elem == 0 ? 4 : 2;
+  struct Part {
+    void **dst;
+    size_t bytes;
+  };
+  std::vector<Part> parts = {
+      {reinterpret_cast<void **>(&h->ids), sizeof(int32_t) * T * k},
+      {reinterpret_cast<void **>(&h->topk_w), sizeof(float) * T * k},
+      {reinterpret_cast<void **>(&h->slot_row), sizeof(int32_t) * T * k},
+      {reinterpret_cast<void **>(&h->perm), sizeof(int32_t) * T * k},
+      {reinterpret_cast<void **>(&h->counts), sizeof(int32_t) * E},
+      {reinterpret_cast<void **>(&h->offsets), sizeof(int32_t) * (E + 1)},
+      {reinterpret_cast<void **>(&h->num_tiles), sizeof(int32_t)},
+      {reinterpret_cast<void **>(&h->tiles), sizeof(afd::Tile) * h->tiles_cap},
+      {reinterpret_cast<void **>(&h->z), static_cast<size_t>(R) * h->zpitch * zes},
+      {reinterpret_cast<void **>(&h->y), static_cast<size_t>(R) * hd * yes},
+  };
+  if (h->elem == 2) {
+    parts.push_back({reinterpret_cast<void **>(&h->xq), static_cast<size_t>(T) * hd});
+    parts.push_back({reinterpret_cast<void **>(&h->xs), sizeof(float) * T * (hd / 128)});
+    parts.push_back(
+        {reinterpret_cast<void **>(&h->zs), sizeof(float) * R * (h->zpitch / 128)});
+  }
+  size_t total = 0;
+  for (auto &p : parts) total = align_up(total, 256) + align_up(p.bytes, 256);
+  hipError_t e = hipMalloc(&h->ws, total);
+  if (e != hipSuccess) {
+    delete h;
+    (void)hipGetLastError();
+    return fail(AFD_ERR_OUT_OF_MEMORY, "workspace of %zu bytes: %s", total, hipGetErrorString(e));
+  }
+  h->ws_bytes = total;
+  size_t off = 0;
+  for (auto &p : parts) {
+    off = align_up(off, 256);
+    *p.dst = static_cast<char *>(h->ws) + off;
+    off += align_up(p.bytes, 256);
+  }
+  *out = h;
+  return AFD_OK;
+}
+
+void afd_ffn_destroy(afd_ffn_handle *h) {
+  if (!h) return;
+  int cur = 0;
+  hipGetDevice(&cur);
+  hipSetDevice(h->device);
+  hipDeviceSynchronize();
+  for (auto &e : h->ev_pool) {
+    hipEventDestroy(e.start);
+    hipEventDestroy(e.stop);
+  }
+  hipFree(h->ws);
+  hipSetDevice(cur);
+  delete h;
+}
+
+static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
+                        hipStream_t s) {
+  if (!h) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  const afd_ffn_config &c = h->cfg;
+  if (T < 0) return fail(AFD_ERR_INVALID_ARG, "T = %lld < 0", static_cast<long long>(T));
+  if (T > c.max_tokens)
+    return fail(AFD_ERR_CAPACITY, "T = %lld exceeds max_tokens = %d", static_cast<long long>(T),
+                c.max_tokens);
+  if (T == 0) return AFD_OK;
+  if (!hidden || !out) return fail(AFD_ERR_INVALID_ARG, "hidden and out must not be NULL");
+  const int aes = h->elem == 0 ? 4 : 2;
+  const size_t act_bytes = static_cast<size_t>(T) * c.hidden * aes;
+  const char *hb = static_cast<const char *>(hidden);
+  const char *ob = static_cast<const char *>(out);
+  if (hb < ob + act_bytes && ob < hb + act_bytes)
+    return fail(AFD_ERR_INVALID_ARG, "hidden and out overlap");
+  int cur = -1;
+  hipGetDevice(&cur);
+  if (cur != h->device)
+    return fail(AFD_ERR_INVALID_ARG, "current device %d is not the handle's device %d", cur,
+                h->device);
+
+  const int Ti = static_cast<int>(T), k = c.top_k, E = c.num_experts, S = c.num_shared;
+  const int hd = c.hidden;
+  const int Tk = Ti * k;
+  hipError_t e;
+  hipEvent_t *ev;
+
+  ev = prof_begin(h, AFD_STAGE_ROUTER, s);
+  e = afd::launch_router(h->elem == 0, hidden, h->w.router_w,
+                         c.has_router_bias ? h->w.router_b : nullptr, Ti, hd, E, k, h->ids,
+                         h->topk_w, s);
+  prof_end(ev, s);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+
+  ev = prof_begin(h, AFD_STAGE_DISPATCH, s);
+  e = afd::launch_dispatch(h->ids, Ti, k, E, S, h->bm, h->counts, h->offsets, h->perm,
+                           h->slot_row, h->tiles, h->num_tiles, s);
+  prof_end(ev, s);
+  if (e != hipSuccess) return hip_fail(e, "dispatch launch");
+
+  const uint8_t *A = static_cast<const uint8_t *>(hidden);
+  int64_t a_pitch = static_cast<int64_t>(hd) * aes;
+  if (h->elem == 2) {
+    ev = prof_begin(h, AFD_STAGE_QUANT, s);
+    e = afd::launch_quant_1x128(static_cast<const uint16_t *>(hidden), T, hd, h->xq, h->xs, s);
+    prof_end(ev, s);
+    if (e != hipSuccess) return hip_fail(e, "quantiser launch");
+    A = h->xq;
+    a_pitch = hd;
+  }
+
+  const int zes = h->elem == 0 ? 4 : (h->elem == 1 ? 2 : 1);
+  const int yes = h->elem == 0 ? 4 : 2;
+  afd::GemmArgs g{};
+  g.A = A;
+  g.a_pitch = a_pitch;
+  g.perm = h->perm;
+  g.a_scale = h->xs;
+  g.a_scale_pitch = hd / 128;
+  g.Tk = Tk;
+  g.T = Ti;
+  g.b0 = static_cast<const uint8_t *>(h->w.gate_w);
+  g.b1 = static_cast<const uint8_t *>(h->w.up_w);
+  g.sb0 = static_cast<const uint8_t *>(h->w.sh_gate_w);
+  g.sb1 = static_cast<const uint8_t *>(h->w.sh_up_w);
+  g.bs0 = h->w.gate_s;
+  g.bs1 = h->w.up_s;
+  g.sbs0 = h->w.sh_gate_s;
+  g.sbs1 = h->w.sh_up_s;
+  g.N = c.inter;
+  g.K = hd;
+  g.Ns = S > 0 ? c.shared_inter : c.inter;
+  g.Ks = hd;
+  g.E = E;
+  g.tiles = h->tiles;
+  g.num_tiles = h->num_tiles;
+  g.tiles_ub = static_cast<int>(tiles_upper_bound(T, k, E, S, h->bm));
+  g.C = h->z;
+  g.c_pitch = static_cast<int64_t>(h->zpitch) * zes;
+  g.c_scale = h->zs;
+  g.c_scale_pitch = h->zpitch / 128;
+  ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
+  e = afd::launch_gemm(afd::GemmKind::GateUp, h->elem, h->bm, g, s);
+  prof_end(ev, s);
+  if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
+
+  afd::GemmArgs d = g;
+  d.A = h->z;
+  d.a_pitch = static_cast<int64_t>(h->zpitch) * zes;
+  d.perm = nullptr;
+  d.a_scale = h->zs;
+  d.a_scale_pitch = h->zpitch / 128;
+  d.b0 = static_cast<const uint8_t *>(h->w.down_w);
+  d.b1 = nullptr;
+  d.sb0 = static_cast<const uint8_t *>(h->w.sh_down_w);
+  d.sb1 = nullptr;
+  d.bs0 = h->w.down_s;
+  d.bs1 = nullptr;
+  d.sbs0 = h->w.sh_down_s;
+  d.sbs1 = nullptr;
+  d.N = hd;
+  d.K = c.inter;
+  d.Ns = hd;
+  d.Ks = S > 0 ? c.shared_inter : c.inter;
+  d.C = h->y;
+  d.c_pitch = static_cast<int64_t>(hd) * yes;
+  d.c_scale = nullptr;
+  ev = prof_begin(h, AFD_STAGE_DOWN, s);
+  e = afd::launch_gemm(afd::GemmKind::Down, h->elem, h->bm, d, s);
+  prof_end(ev, s);
+  if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
+
+  ev = prof_begin(h, AFD_STAGE_COMBINE, s);
+  e = afd::launch_combine(h->elem == 0, h->y, h->slot_row, h->topk_w, Ti, k, S, hd, out, s);
+  prof_end(ev, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return AFD_OK;
+}
+
+int afd_ffn_forward(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
+                    afd_stream_t stream) {
+  return forward_impl(h, hidden, out, T, static_cast<hipStream_t>(stream));
+}
+
+int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
+                           afd_stream_t stream, const afd_ffn_trace *tr) {
+  if (!tr) return fail(AFD_ERR_INVALID_ARG, "trace is NULL");
+  if (h && T > 0 && (tr->x_q || tr->x_s) && h->elem != 2)
+    return fail(AFD_ERR_INVALID_ARG, "x_q / x_s are only produced in W8A8 mode");
+  int rc = forward_impl(h, hidden, out, T, static_cast<hipStream_t>(stream));
+  if (rc || T == 0) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const afd_ffn_config &c = h->cfg;
+  const size_t tk = static_cast<size_t>(T) * c.top_k;
+  struct Cp {
+    void *dst;
+    const void *src;
+    size_t bytes;
+  } cps[] = {
+      {tr->topk_ids, h->ids, tk * 4},
+      {tr->topk_w, h->topk_w, tk * 4},
+      {tr->counts, h->counts, static_cast<size_t>(c.num_experts) * 4},
+      {tr->offsets, h->offsets, static_cast<size_t>(c.num_experts + 1) * 4},
+      {tr->perm, h->perm, tk * 4},
+      {tr->slot_row, h->slot_row, tk * 4},
+      {tr->x_q, h->xq, static_cast<size_t>(T) * c.hidden},
+      {tr->x_s, h->xs, static_cast<size_t>(T) * (c.hidden / 128) * 4},
+  };
+  for (auto &cp : cps) {
+    if (!cp.dst) continue;
+    hipError_t e = hipMemcpyAsync(cp.dst, cp.src, cp.bytes, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "trace copy");
+  }
+  return AFD_OK;
+}
+
+int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols, uint8_t *q, float *s,
+                        afd_stream_t stream) {
+  if (!x || !q || !s) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");
+  if (rows < 0 || cols <= 0 || cols % 128)
+    return fail(AFD_ERR_INVALID_ARG, "rows >= 0 and cols a positive multiple of 128 required");
+  if (rows == 0) return AFD_OK;
+  if (rows * (cols / 128) * 16 / 256 >= (1LL << 31))
+    return fail(AFD_ERR_UNSUPPORTED, "tensor too large for one launch");
+  hipError_t e = afd::launch_quant_1x128(static_cast<const uint16_t *>(x), rows, cols, q, s,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AFD_OK : hip_fail(e, "quantiser launch");
+}
+
+int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols, uint8_t *q, float *s,
+                          afd_stream_t stream) {
+  if (!w || !q || !s) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");
+  if (rows <= 0 || cols <= 0 || rows % 128 || cols % 128)
+    return fail(AFD_ERR_INVALID_ARG, "rows and cols must be positive multiples of 128");
+  if ((rows / 128) * (cols / 128) >= (1LL << 31))
+    return fail(AFD_ERR_UNSUPPORTED, "tensor too large for one launch");
+  hipError_t e = afd::launch_quant_128x128(static_cast<const uint16_t *>(w), rows, cols, q, s,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AFD_OK : hip_fail(e, "quantiser launch");
+}
+
+int afd_ffn_profile_enable(afd_ffn_handle *h, uint32_t stage_mask) {
+  if (!h) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
+  if (stage_mask >> AFD_STAGE_COUNT) return fail(AFD_ERR_INVALID_ARG, "unknown stage bits");
+  h->prof_mask = stage_mask;
+  return AFD_OK;
+}
+
+int afd_ffn_profile_read(afd_ffn_handle *h, double *ms, int64_t *launches) {
+  if (!h || !ms || !launches) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");
+  for (int i = 0; i < AFD_STAGE_COUNT; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  for (size_t i = 0; i < h->ev_used; ++i) {
+    hipError_t e = hipEventSynchronize(h->ev_pool[i].stop);
+    if (e != hipSuccess) return hip_fail(e, "profile event");
+    float t = 0.0f;
+    e = hipEventElapsedTime(&t, h->ev_pool[i].start, h->ev_pool[i].stop);
+    if (e != hipSuccess) return hip_fail(e, "profile event");
+    ms[h->ev_stage[i]] += t;
+    launches[h->ev_stage[i]] += 1;
+  }
+  h->ev_used = 0;
+  return AFD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace afd {
+
+// One GEMM work tile: `rows` (<= BM) consecutive dispatched rows starting at
+// `row0`, all belonging to `group` (< E: routed expert, >= E: shared expert
+// group - E).  Built on the device by the dispatch kernel.
+struct Tile {
+  int32_t group;
+  int32_t row0;
+  int32_t rows;
+  int32_t pad;
+};
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxShared = 8;
+
+// Router GEMM + softmax + top-k + renormalisation.
+// f32: x, wr are fp32; else bf16.  bias may be null.
+hipError_t launch_router(bool f32, const void *x, const void *wr,
+                         const float *bias, int T, int h, int E, int k,
+                         int32_t *ids, float *w, hipStream_t s);
+
+// Histogram, scan and stable scatter of the (token, slot) pairs; GEMM tile
+// list for row tiles of `bm` rows (routed experts, then S shared groups).
+hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
+                           int bm, int32_t *counts, int32_t *offsets,
+                           int32_t *perm, int32_t *slot_row, Tile *tiles,
+                           int32_t *num_tiles, hipStream_t s);
+
+hipError_t launch_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
+                              uint8_t *q, float *sc, hipStream_t s);
+hipError_t launch_quant_128x128(const uint16_t *w, int64_t rows,
+                                int64_t cols, uint8_t *q, float *sc,
+                                hipStream_t s);
+
+enum class GemmKind { GateUp = 0, Down = 1 };
+
+// Grouped GEMM over the tile list.  Element type: 0 f32, 1 bf16, 2 fp8.
+struct GemmArgs {
+  // A operand: rows of `A` (row pitch a_pitch bytes).  For GateUp the row of
+  // a routed dispatched row r is perm[r], of a shared row it is the token;
+  // for Down it is r itself.
+  const uint8_t *A;
+  int64_t a_pitch;
+  const int32_t *perm;
+  const float *a_scale;  // fp8: [rows of A, a_scale_pitch]
+  int a_scale_pitch;
+  int Tk, T;             // routed rows, tokens
+  // B operand (weights [N, K] per group).  b0 = gate (GateUp) or down;
+  // b1 = up (GateUp only).  Shared experts use sb0 / sb1.
+  const uint8_t *b0, *b1, *sb0, *sb1;
+  const float *bs0, *bs1, *sbs0, *sbs1;  // fp8 block scales
+  int N, K, Ns, Ks;      // routed and shared dims
+  int E;
+  const Tile *tiles;
+  const int32_t *num_tiles;
+  int tiles_ub;          // upper bound of the tile count (grid sizing)
+  // C: output rows indexed by dispatched row, pitch c_pitch bytes.
+  uint8_t *C;
+  int64_t c_pitch;
+  float *c_scale;        // fp8 GateUp: [R, c_scale_pitch]
+  int c_scale_pitch;
+};
+
+// Tile height (rows per tile) the GEMMs of a mode use for T tokens; the
+// dispatch kernel builds the tile list with the same value.
+int gemm_bm(int elem, int T, int k, int E);
+
+hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,
+                       hipStream_t s);
+
+// out[t] = sum_j w[t,j] Y[slot_row[t,j]] + sum_s Y[Tk + s*T + t].
+hipError_t launch_combine(bool f32, const uint8_t *Y, const int32_t *slot_row,
+                          const float *w, int T, int k, int S, int h,
+                          void *out, hipStream_t s);
+
+}  // namespace afd

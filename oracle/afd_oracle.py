@@ -89,9 +89,6 @@ def e4m3_positive_grid() -> np.ndarray:
     return e4m3_decode(np.arange(0x7F, dtype=np.uint8))
 
 
-_GRID = None
-
-
 def e4m3_encode(v: np.ndarray) -> np.ndarray:
     """Encode fp32 values to E4M3FN codes.
 
@@ -101,18 +98,19 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     the spacing (a power of two, exact) and rounding half-to-even gives the
     grid point; an even multiple of the spacing is an even mantissa.  The
     sign bit of the input is kept, also for results of zero."""
-    global _GRID
-    if _GRID is None:
-        _GRID = e4m3_positive_grid()
     x = np.asarray(v, dtype=np.float32).astype(np.float64)
     neg = np.signbit(x)
     a = np.minimum(np.abs(x), E4M3_MAX)
     _, p = np.frexp(a)                       # a = f 2^p, f in [0.5, 1)
-    spacing = np.where(a >= 2.0 ** -6, np.ldexp(1.0, (p - 1 - 3).astype(np.int64)),
-                       2.0 ** -9)
-    r = np.rint(a / spacing) * spacing       # exact: spacing is a power of 2
-    code = np.searchsorted(_GRID, r).astype(np.uint8)
-    assert np.all(_GRID[code] == r)
+    e = (p - 1).astype(np.int64)             # a in [2^e, 2^(e+1))
+    normal = a >= 2.0 ** -6
+    spacing = np.where(normal, np.ldexp(1.0, e - 3), 2.0 ** -9)
+    n = np.rint(a / spacing)                 # exact division, ties to even
+    # normal: value n * 2^(e-3), n in [8, 16] -> exponent field e + 7 and
+    # mantissa n - 8 (n = 16 is mantissa 0 of the next binade, i.e. the
+    # next code); subnormal: the code is n itself (n = 8 is 2^-6, code 8).
+    code = np.where(normal, (e + 7) * 8 + (n.astype(np.int64) - 8),
+                    n.astype(np.int64)).astype(np.uint8)
     return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
 
 
@@ -153,15 +151,26 @@ def quantize_128x128(w: np.ndarray):
     return e4m3_encode(v).reshape(R, C), s
 
 
+_DECODE_TABLE = None
+
+
+def _decode_fast(q: np.ndarray) -> np.ndarray:
+    """e4m3_decode through a 256-entry table of its own results."""
+    global _DECODE_TABLE
+    if _DECODE_TABLE is None:
+        _DECODE_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))
+    return _DECODE_TABLE[np.asarray(q, np.uint8)]
+
+
 def dequantize_1x128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     R, C = q.shape
-    return (e4m3_decode(q).reshape(R, C // 128, 128)
+    return (_decode_fast(q).reshape(R, C // 128, 128)
             * s.astype(np.float64)[..., None]).reshape(R, C)
 
 
 def dequantize_128x128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     R, C = q.shape
-    return (e4m3_decode(q).reshape(R // 128, 128, C // 128, 128)
+    return (_decode_fast(q).reshape(R // 128, 128, C // 128, 128)
             * s.astype(np.float64)[:, None, :, None]).reshape(R, C)
 
 
@@ -245,8 +254,9 @@ class OracleFFN:
     ``router_weight()``, ``router_bias()``, ``expert(e)`` -> (gate, up, down)
     and ``shared(j)``; ``shape`` has the sizes (h, E, k, I, S, Is, mode)."""
 
-    def __init__(self, src, shape=None):
+    def __init__(self, src, shape=None, threads: int = 1):
         self.src = src
+        self.threads = max(1, int(threads))
         self.shape = shape if shape is not None else src.shape
         s = self.shape
         assert 1 <= s.k <= s.E
@@ -306,14 +316,24 @@ class OracleFFN:
         n = x_all.shape[0]
         quant_z = s.mode == "w8a8"
         routed = np.zeros((n, s.h), np.float64)
-        # y of every (token, slot), experts visited in index order
+        # y of every (token, slot); experts are independent, so they may be
+        # evaluated by several threads (each writes its own (t, j) slots)
         y_slot = np.zeros((n, s.k, s.h), np.float64)
-        for e in range(s.E):
+
+        def run_expert(e):
             hit = np.nonzero(ids == e)
             if hit[0].size == 0:
-                continue
+                return
             G, U, D = self._weights(self.src.expert(e))
             y_slot[hit[0], hit[1]] = swiglu(xin[hit[0]], G, U, D, quant_z)
+
+        if self.threads == 1:
+            for e in range(s.E):
+                run_expert(e)
+        else:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(self.threads) as ex:
+                list(ex.map(run_expert, range(s.E)))
         routed = np.einsum("tj,tjh->th", w, y_slot)
         out = routed.copy()
         for j in range(s.S):

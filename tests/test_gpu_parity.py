@@ -1,0 +1,237 @@
+"""HIP path vs fp64 oracle on small layers that still span several row and
+column tiles, ragged tails, empty experts, several shared experts, every
+router variant and all three precisions.  Calls go through the C ABI
+(ctypes binding).  GPU only."""
+import numpy as np
+import pytest
+import torch
+
+from afd_inputs import CONFIGS, LayerShape, SyntheticLayer, f32_to_bf16_bits, tie_case
+from oracle import afd_oracle as O
+
+from parity import (TOL, check_dispatch, check_outputs, check_routing, decode_store,
+                    routing_slack)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _np(t):
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return O.bf16_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+    return t.numpy()
+
+
+def run_gpu(syn, x_store=None, max_tokens=None, layer=None):
+    from expert_side_attention_amd.workload import build_layer, to_device
+    s = syn.shape
+    layer = layer or build_layer(syn, DEV, max_tokens=max_tokens)
+    x = syn.hidden() if x_store is None else x_store
+    xt = to_device(x, DEV, s.mode != "f32")
+    out, tr = layer.forward(xt, trace=True)
+    torch.cuda.synchronize()
+    return layer, _np(out), {k: v.cpu().numpy() for k, v in tr.items()}
+
+
+def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False):
+    s = syn.shape
+    x = syn.hidden() if x_store is None else x_store
+    print(f"[parity] {s}", flush=True)
+    _, out, tr = run_gpu(syn, x)
+    orc = O.OracleFFN(syn, threads=threads)
+    ref = orc.forward(x)
+    x64 = decode_store(x, s.mode)
+    beta = routing_slack(x64, orc._wr, orc._b, s.h)
+    differ = check_routing(ref["logits"], beta, tr["topk_ids"], s.k)
+    if expect_exact_routing:
+        assert not differ.any()
+    assert differ.mean() <= 0.01, f"{differ.sum()} tokens route differently"
+    check_dispatch(tr, s.E)
+    same = ~differ
+    assert np.allclose(tr["topk_w"][same], ref["w"][same], rtol=0, atol=2e-6)
+    if s.mode == "w8a8":
+        assert np.array_equal(tr["x_q"], ref["x_q"])
+        assert np.array_equal(tr["x_s"], ref["x_s"])
+    rel, mabs = check_outputs(out, ref["out"], s.mode, keep=same)
+    print(f"[parity] rel-L2 {rel:.3e} max-abs/max {mabs:.3e} "
+          f"near-tie tokens {int(differ.sum())}", flush=True)
+    return out, tr, ref
+
+
+SMALL = [
+    # name, shape
+    CONFIGS["tiny_fp32"],
+    LayerShape("bf16_ragged", T=300, h=256, E=8, k=3, I=384, S=1, Is=256, mode="bf16"),
+    LayerShape("bf16_many_experts", T=77, h=512, E=64, k=8, I=256, S=2, Is=128, mode="bf16"),
+    LayerShape("bf16_e256", T=40, h=128, E=256, k=8, I=128, mode="bf16"),
+    LayerShape("bf16_e512", T=20, h=128, E=512, k=4, I=128, S=1, Is=128, mode="bf16"),
+    LayerShape("bf16_zipf", T=500, h=256, E=32, k=4, I=128, S=1, Is=128, mode="bf16",
+               router="zipf"),
+    LayerShape("bf16_big_t", T=2100, h=128, E=64, k=2, I=128, mode="bf16"),
+    LayerShape("f32_k_eq_e", T=70, h=128, E=4, k=4, I=128, S=1, Is=256, mode="f32"),
+    LayerShape("w8a8_small", T=200, h=512, E=8, k=2, I=256, S=1, Is=384, mode="w8a8"),
+    LayerShape("w8a8_many", T=96, h=256, E=32, k=8, I=384, mode="w8a8"),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=[s.name for s in SMALL])
+def test_small_layer_parity(shape):
+    check_layer(SyntheticLayer(shape, seed=3))
+
+
+def test_tiny_fp32_is_fp32_accurate():
+    out, tr, ref = check_layer(SyntheticLayer(CONFIGS["tiny_fp32"], seed=0),
+                               expect_exact_routing=True)
+    rel = np.linalg.norm(out - ref["out"]) / np.linalg.norm(ref["out"])
+    assert rel < 1e-5, rel
+
+
+def test_exact_ties_pick_lowest_index():
+    shape = LayerShape("ties", T=64, h=256, E=16, k=4, I=128, mode="bf16")
+    syn = SyntheticLayer(shape, seed=4)
+    x, wr = tie_case(T=64, h=256, E=16, seed=4)
+
+    class Src:
+        pass
+    src = Src()
+    src.shape = shape
+    src.router_weight = lambda: wr
+    src.router_bias = lambda: None
+    src.expert = syn.expert
+    src.shared = syn.shared
+    src.hidden = lambda: x
+    from expert_side_attention_amd.workload import build_layer, to_device
+    layer = build_layer(syn, DEV)
+    # replace the router weight with the integer-valued one
+    layer2 = type(layer)(mode="bf16", hidden=256, num_experts=16, top_k=4, inter=128,
+                         max_tokens=64, router_w=to_device(wr, DEV, True),
+                         gate_w=layer._keep[2], up_w=layer._keep[3], down_w=layer._keep[4])
+    xt = to_device(x, DEV, True)
+    out, tr = layer2.forward(xt, trace=True)
+    torch.cuda.synchronize()
+    ref = O.OracleFFN(src).forward(x)
+    assert np.array_equal(tr["topk_ids"].cpu().numpy(), ref["ids"])
+    l = ref["logits"]
+    assert np.any(l[:, 0] == l[:, 1])  # ties really occur
+
+
+def test_uniform_router_selects_all_in_index_order():
+    shape = LayerShape("uniform", T=33, h=128, E=8, k=8, I=128, mode="bf16")
+    syn = SyntheticLayer(shape, seed=5)
+    from expert_side_attention_amd.workload import build_layer, to_device
+    base = build_layer(syn, DEV)
+    zero = torch.zeros((8, 128), dtype=torch.bfloat16, device=DEV)
+    layer = type(base)(mode="bf16", hidden=128, num_experts=8, top_k=8, inter=128,
+                       max_tokens=33, router_w=zero, gate_w=base._keep[2],
+                       up_w=base._keep[3], down_w=base._keep[4])
+    out, tr = layer.forward(to_device(syn.hidden(), DEV, True), trace=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(tr["topk_ids"].cpu().numpy(), np.tile(np.arange(8), (33, 1)))
+    assert np.allclose(tr["topk_w"].cpu().numpy(), 0.125, atol=1e-7)
+
+
+def test_determinism_and_microbatch_split():
+    shape = LayerShape("split", T=257, h=256, E=16, k=4, I=256, S=1, Is=128, mode="bf16")
+    syn = SyntheticLayer(shape, seed=6)
+    from expert_side_attention_amd.workload import build_layer, to_device
+    layer = build_layer(syn, DEV)
+    xt = to_device(syn.hidden(), DEV, True)
+    a = layer.forward(xt).clone()
+    b = layer.forward(xt).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # rows of a token never mix with other tokens' rows, so a split batch
+    # gives the same bits per token
+    p1 = layer.forward(xt[:100].contiguous()).clone()
+    p2 = layer.forward(xt[100:].contiguous()).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([p1, p2]).view(torch.int16), a.view(torch.int16))
+
+
+def test_two_streams_two_handles_match_serial():
+    shape = LayerShape("streams", T=512, h=256, E=16, k=4, I=256, S=1, Is=256, mode="bf16")
+    syn = SyntheticLayer(shape, seed=7)
+    from expert_side_attention_amd.workload import build_layer, to_device
+    l0 = build_layer(syn, DEV, max_tokens=256)
+    k = l0._keep
+    l1 = type(l0)(mode="bf16", hidden=256, num_experts=16, top_k=4, inter=256,
+                  max_tokens=256, router_w=k[0], gate_w=k[2], up_w=k[3], down_w=k[4],
+                  num_shared=1, shared_inter=256, sh_gate_w=k[8], sh_up_w=k[9],
+                  sh_down_w=k[10])
+    xt = to_device(syn.hidden(), DEV, True)
+    serial = torch.cat([l0.forward(xt[:256].contiguous()), l0.forward(xt[256:].contiguous())])
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    x0, x1 = xt[:256].contiguous(), xt[256:].contiguous()
+    o0, o1 = torch.empty_like(x0), torch.empty_like(x1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        l0.forward(x0, out=o0, stream=s0)
+        l1.forward(x1, out=o1, stream=s1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o0, o1]).view(torch.int16), serial.view(torch.int16))
+
+
+def test_edge_token_counts_and_errors():
+    from expert_side_attention_amd import AfdError
+    from expert_side_attention_amd.workload import build_layer, to_device
+    shape = LayerShape("edges", T=64, h=128, E=8, k=2, I=128, S=1, Is=128, mode="bf16")
+    syn = SyntheticLayer(shape, seed=8)
+    layer = build_layer(syn, DEV, max_tokens=64)
+    xt = to_device(syn.hidden(), DEV, True)
+    full = layer.forward(xt).clone()
+    one = layer.forward(xt[:1].contiguous()).clone()
+    empty = layer.forward(xt[:0].contiguous())
+    torch.cuda.synchronize()
+    assert empty.shape == (0, 128)
+    assert torch.equal(one.view(torch.int16), full[:1].view(torch.int16))
+    big = torch.zeros((65, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(AfdError) as ei:
+        layer.forward(big)
+    assert ei.value.status == 3  # AFD_ERR_CAPACITY
+    with pytest.raises(AfdError) as ei:
+        layer.forward(xt, out=xt)
+    assert ei.value.status == 1  # aliasing
+
+
+def test_quantiser_all_bf16_values():
+    """Every finite bf16 value through the 1x128 quantiser, in rows whose
+    group maxima span the whole range (so results land on every E4M3
+    binade, subnormals and zero included): codes and scales bit-exact."""
+    from expert_side_attention_amd import quantize_fp8_1x128
+    from expert_side_attention_amd.workload import to_device
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (allv >> 7) & 0xFF
+    vals = allv[exp != 0xFF]                        # drop Inf/NaN
+    g = np.random.default_rng(0)
+    rows = []
+    for rep in range(2):
+        p = g.permutation(vals)
+        rows.append(p[: (len(p) // 128) * 128].reshape(-1, 128))
+    x = np.concatenate(rows)
+    x[::7, 5] = 0x0000          # zeros
+    x[::11, :] = 0x8000         # all negative-zero rows -> scale 1
+    xt = to_device(x, DEV, True)
+    q, s = quantize_fp8_1x128(xt)
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_1x128(O.bf16_to_f64(x).astype(np.float32))
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+def test_block_quantiser_matches_oracle():
+    from expert_side_attention_amd import quantize_fp8_128x128
+    from expert_side_attention_amd.workload import to_device
+    g = np.random.default_rng(1)
+    w = (g.standard_normal((3, 256, 384)) * 0.02).astype(np.float32)
+    w[1, :128, 128:256] *= 1e-30                    # tiny block
+    w[2, 128:, :128] = 0                            # zero block
+    wb = f32_to_bf16_bits(w)
+    q, s = quantize_fp8_128x128(to_device(wb, DEV, True))
+    torch.cuda.synchronize()
+    for e in range(3):
+        rq, rs = O.quantize_128x128(O.bf16_to_f64(wb[e]).astype(np.float32))
+        assert np.array_equal(q[e].cpu().numpy(), rq)
+        assert np.array_equal(s[e].cpu().numpy(), rs)
