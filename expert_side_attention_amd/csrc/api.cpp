@@ -52,11 +52,10 @@ struct afd_ffn_handle {
   int device;
   int elem;    // 0 f32, 1 bf16, 2 fp8 (GEMM operand type)
   int zpitch;  // Z row length in elements: max(I, I_s)
-  int bm;      // row tile height
   int tiles_cap;
   void *ws;
   size_t ws_bytes;
-  int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles;
+  int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *counters;
   float *topk_w;
   afd::Tile *tiles;
   uint8_t *xq;
@@ -172,7 +171,6 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
   h->zpitch = (S > 0 && cfg->shared_inter > cfg->inter) ? cfg->shared_inter : cfg->inter;
   const int64_t T = cfg->max_tokens, k = cfg->top_k, E = cfg->num_experts;
   const int64_t hd = cfg->hidden;
-  h->bm = afd::gemm_bm(h->elem, cfg->max_tokens, cfg->top_k, cfg->num_experts);
   h->tiles_cap = static_cast<int>(tiles_upper_bound(T, cfg->top_k, cfg->num_experts, S, 16));
 
   const int64_t R = T * k + S * T;  // dispatched + shared rows
@@ -190,6 +188,7 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
       {reinterpret_cast<void **>(&h->counts), sizeof(int32_t) * E},
       {reinterpret_cast<void **>(&h->offsets), sizeof(int32_t) * (E + 1)},
       {reinterpret_cast<void **>(&h->num_tiles), sizeof(int32_t)},
+      {reinterpret_cast<void **>(&h->counters), 2 * sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->tiles), sizeof(afd::Tile) * h->tiles_cap},
       {reinterpret_cast<void **>(&h->z), static_cast<size_t>(R) * h->zpitch * zes},
       {reinterpret_cast<void **>(&h->y), static_cast<size_t>(R) * hd * yes},
@@ -269,9 +268,10 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
 
+  const afd::GemmPlan plan = afd::gemm_plan(h->elem, Ti, k, E);
   ev = prof_begin(h, AFD_STAGE_DISPATCH, s);
-  e = afd::launch_dispatch(h->ids, Ti, k, E, S, h->bm, h->counts, h->offsets, h->perm,
-                           h->slot_row, h->tiles, h->num_tiles, s);
+  e = afd::launch_dispatch(h->ids, Ti, k, E, S, plan.bm, h->counts, h->offsets, h->perm,
+                           h->slot_row, h->tiles, h->num_tiles, h->counters, 2, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
 
@@ -311,13 +311,15 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   g.E = E;
   g.tiles = h->tiles;
   g.num_tiles = h->num_tiles;
-  g.tiles_ub = static_cast<int>(tiles_upper_bound(T, k, E, S, h->bm));
+  g.tiles_ub = static_cast<int>(tiles_upper_bound(T, k, E, S, plan.bm));
+  g.work_counter = h->counters;
   g.C = h->z;
   g.c_pitch = static_cast<int64_t>(h->zpitch) * zes;
   g.c_scale = h->zs;
   g.c_scale_pitch = h->zpitch / 128;
   ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
-  e = afd::launch_gemm(afd::GemmKind::GateUp, h->elem, h->bm, g, s);
+  e = plan.stream ? afd::launch_gemm_stream(afd::GemmKind::GateUp, h->elem, plan.bm, g, s)
+                  : afd::launch_gemm(afd::GemmKind::GateUp, h->elem, plan.bm, g, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
 
@@ -342,8 +344,10 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   d.C = h->y;
   d.c_pitch = static_cast<int64_t>(hd) * yes;
   d.c_scale = nullptr;
+  d.work_counter = h->counters + 1;
   ev = prof_begin(h, AFD_STAGE_DOWN, s);
-  e = afd::launch_gemm(afd::GemmKind::Down, h->elem, h->bm, d, s);
+  e = plan.stream ? afd::launch_gemm_stream(afd::GemmKind::Down, h->elem, plan.bm, d, s)
+                  : afd::launch_gemm(afd::GemmKind::Down, h->elem, plan.bm, d, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
 

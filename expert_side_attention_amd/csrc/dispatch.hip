@@ -54,7 +54,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     const int32_t *__restrict__ ids, int T, int k, int E, int S, int bm,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, int32_t *__restrict__ slot_row,
-    Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles) {
+    Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles,
+    int32_t *__restrict__ counters, int ncounters) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int run[kMaxExperts];
   __shared__ unsigned long long mask[kWaves][kMaxExperts];
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     tiles[routed_tiles + i] = t;
   }
   if (tid == 0) *num_tiles = routed_tiles + S * ns;
+  if (tid < ncounters) counters[tid] = 0;
   __syncthreads();
 
   // 3. stable scatter, 1024 tokens per pass
@@ -140,9 +142,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
                            int bm, int32_t *counts, int32_t *offsets,
                            int32_t *perm, int32_t *slot_row, Tile *tiles,
-                           int32_t *num_tiles, hipStream_t s) {
+                           int32_t *num_tiles, int32_t *counters,
+                           int ncounters, hipStream_t s) {
   dispatch_kernel<<<1, kThreads, 0, s>>>(ids, T, k, E, S, bm, counts, offsets,
-                                         perm, slot_row, tiles, num_tiles);
+                                         perm, slot_row, tiles, num_tiles,
+                                         counters, ncounters);
   return hipGetLastError();
 }
 

@@ -295,11 +295,14 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
-int gemm_bm(int elem, int T, int k, int E) {
-  (void)T;
-  (void)k;
-  (void)E;
-  return elem == 0 ? 32 : 64;
+GemmPlan gemm_plan(int elem, int T, int k, int E) {
+  if (elem == 0) return {32, false};
+  // rows per expert on average decide the regime: a few dozen rows per
+  // expert -> stream the weights once with a tile that holds all of them
+  const int64_t avg = (static_cast<int64_t>(T) * k + E - 1) / E;
+  if (avg <= 48) return {64, true};
+  if (avg <= 112) return {128, true};
+  return {64, false};
 }
 
 hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,

@@ -1,0 +1,360 @@
+// Weight-streaming grouped expert GEMMs (gate/up + SwiGLU, and down) for the
+// decode regime, where every expert sees only a few dozen rows and the time
+// goes into reading each expert's weights once from HBM.  Experts are large,
+// sparsely activated matrix products (A/F 分离 page, "为什么要拆"); at
+// decode batch sizes their cost is the weight bytes.
+//
+// Design (gfx950, wave64):
+//  * Persistent workgroups claim work items (row tile x column tile) from a
+//    device counter that the dispatch kernel zeroes, so the grid never
+//    depends on host-side counts and the tail is one item long.
+//  * Each wave owns 16 weight rows of each matrix (gate and up, or down).
+//    Weights go from global memory straight into MFMA operand registers,
+//    one "super-stage" (SS bytes of K per row) ahead of the math: no LDS
+//    round trip and no barrier on the weight path.  Load instruction i of a
+//    super-stage reads bytes [64 i, 64 i + 64) of 16 rows (lane group
+//    q = lane/16 takes 16 bytes at 64 i + 16 q), so every instruction moves
+//    whole 64-byte row segments.
+//  * The gathered activation rows (a few KB per tile, shared by all waves)
+//    are staged through LDS, double-buffered per super-stage.
+//  * bf16: chunk i is one 16x16x32 MFMA.  fp8: chunks 2b and 2b+1 (bytes
+//    [128 b + 16 q] and [128 b + 64 + 16 q]) lie in the same 128-wide K
+//    block b and feed one 16x16x128 MFMA; the block's partial sum is then
+//    scaled by (activation scale of the row) x (weight block scale).
+//    A and B use the same byte->K assignment, so the products are exact
+//    permutations of the K sum.
+//  * Epilogues stage the tile through LDS and write whole 16-byte pieces;
+//    the fp8 gate/up epilogue quantises z per row per 128 columns.
+#include "common.h"
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace afd {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
+struct StreamCfg {
+  static constexpr int kThreads = WAVES * 64;
+  static constexpr int NMAT = SWIGLU ? 2 : 1;
+  static constexpr int BN = 16 * WAVES;       // columns per matrix per item
+  static constexpr int MB = BM / 16;
+  static constexpr int NCH = SS / 64;         // 16-byte chunks per lane per row block
+  static constexpr int NPR = NCH / 2;         // chunk pairs (one fp8 K block each)
+  static constexpr int APITCH = SS + 16;      // LDS row pitch of the A stage
+  static constexpr int ACH = BM * SS / 16;    // 16-byte chunks of one A stage
+  static constexpr int RA = (ACH + kThreads - 1) / kThreads;
+  static constexpr int KB = SS / 128;         // fp8 scale blocks per super-stage
+  static constexpr bool FP8 = EL == Elem::FP8;
+  static constexpr int LDS_A = 2 * BM * APITCH;
+  // epilogue staging: BM rows x BN columns of the output element
+  static constexpr int OUT_ES = FP8 && SWIGLU ? 1 : 2;
+  static constexpr int LDS_OUT = BM * BN * OUT_ES;
+  static constexpr int LDS = LDS_A > LDS_OUT ? LDS_A : LDS_OUT;
+  static_assert(BM % 16 == 0 && SS % 128 == 0, "shape");
+  static_assert(!FP8 || BN == 128, "fp8: one weight scale block row per item");
+};
+
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
+__global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs p) {
+  using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU>;
+  constexpr int NMAT = C::NMAT, BN = C::BN, MB = C::MB, NCH = C::NCH;
+  constexpr int APITCH = C::APITCH, ACH = C::ACH, RA = C::RA, KB = C::KB;
+  constexpr int THREADS = C::kThreads;
+
+  __shared__ __align__(16) uint8_t lds[C::LDS];
+  __shared__ int rowsrc[BM];
+  __shared__ float sAs[2][C::FP8 ? BM * KB : 1];
+  __shared__ float red[C::FP8 && SWIGLU ? WAVES * BM : 1];
+  __shared__ int s_item;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int nmax = p.N > p.Ns ? p.N : p.Ns;
+  const int ntn = nmax / BN;
+
+  for (;;) {
+    __syncthreads();  // every thread has read the previous s_item
+    if (tid == 0) s_item = atomicAdd(p.work_counter, 1);
+    __syncthreads();
+    const int item = s_item;
+    const int total = *p.num_tiles * ntn;
+    if (item >= total) break;
+    const Tile tile = p.tiles[item / ntn];
+    const int nt = item % ntn;
+    const bool shared = tile.group >= p.E;
+    const int N = shared ? p.Ns : p.N;
+    const int K = shared ? p.Ks : p.K;
+    const int n0 = nt * BN;
+    if (n0 >= N) continue;  // uniform over the workgroup
+    const int g = shared ? tile.group - p.E : tile.group;
+    const int rows = tile.rows;
+    if (tid < BM) {
+      int src = -1;
+      if (tid < rows) {
+        const int r = tile.row0 + tid;
+        src = p.perm ? (r < p.Tk ? p.perm[r] : (r - p.Tk) % p.T) : r;
+      }
+      rowsrc[tid] = src;
+    }
+    __syncthreads();
+
+    const int ES = C::FP8 ? 1 : 2;
+    const int64_t krow = static_cast<int64_t>(K) * ES;
+    const int nss = static_cast<int>(krow / SS);
+    const int64_t mat = static_cast<int64_t>(N) * krow;
+    const uint8_t *bptr[NMAT];
+    {
+      const uint8_t *b0 = (shared ? p.sb0 : p.b0) + g * mat;
+      bptr[0] = b0 + static_cast<int64_t>(n0 + wave * 16 + r16) * krow + q * 16;
+      if constexpr (SWIGLU) {
+        const uint8_t *b1 = (shared ? p.sb1 : p.b1) + g * mat;
+        bptr[NMAT - 1] = b1 + static_cast<int64_t>(n0 + wave * 16 + r16) * krow + q * 16;
+      }
+    }
+    const float *bsc[NMAT] = {};
+    if constexpr (C::FP8) {
+      const int kblocks = K / 128;
+      const int64_t sblk = static_cast<int64_t>(N / 128) * kblocks;
+      bsc[0] = (shared ? p.sbs0 : p.bs0) + g * sblk + (n0 / 128) * kblocks;
+      if constexpr (SWIGLU) bsc[NMAT - 1] = (shared ? p.sbs1 : p.bs1) + g * sblk + (n0 / 128) * kblocks;
+    }
+    const int mb_active = (rows + 15) >> 4;
+
+    // ---- register buffers: chunk pairs (2c, 2c+1) share one 8-dword
+    // register tuple, which is exactly one fp8 MFMA operand
+    u32x8 bq[2][NMAT][C::NPR];
+    u32x4 ra[RA];
+    float as_reg = 0.0f;
+    auto load_b = [&](u32x8 (&dst)[NMAT][C::NPR], int ss) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < C::NPR; ++c) {
+          const uint8_t *src = bptr[m] + static_cast<int64_t>(ss) * SS + c * 128;
+          dst[m][c].lo = ld16(src);
+          dst[m][c].hi = ld16(src + 64);
+        }
+    };
+    auto load_a = [&](int ss) {
+#pragma unroll
+      for (int i = 0; i < RA; ++i) {
+        const int c = tid + THREADS * i;
+        if (c < ACH) {
+          const int row = c / (SS / 16), col = c % (SS / 16);
+          const int src = rowsrc[row];
+          if (src >= 0)
+            ra[i] = ld16(p.A + src * p.a_pitch + static_cast<int64_t>(ss) * SS + col * 16);
+          else
+            ra[i] = u32x4{0, 0, 0, 0};
+        }
+      }
+      if constexpr (C::FP8) {
+        if (tid < BM * KB) {
+          const int src = rowsrc[tid / KB];
+          as_reg = src >= 0 ? p.a_scale[static_cast<int64_t>(src) * p.a_scale_pitch + ss * KB + tid % KB]
+                            : 0.0f;
+        }
+      }
+    };
+    auto store_a = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < RA; ++i) {
+        const int c = tid + THREADS * i;
+        if (c < ACH) {
+          const int row = c / (SS / 16), col = c % (SS / 16);
+          st16(lds + buf * BM * APITCH + row * APITCH + col * 16, ra[i]);
+        }
+      }
+      if constexpr (C::FP8)
+        if (tid < BM * KB) sAs[buf][tid] = as_reg;
+    };
+
+    f32x4 acc[NMAT][MB];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[m][b] = f32x4{0, 0, 0, 0};
+
+    auto compute = [&](const u32x8 (&bb)[NMAT][C::NPR], int buf, int ss) {
+      const uint8_t *abase = lds + buf * BM * APITCH + r16 * APITCH + q * 16;
+      if constexpr (!C::FP8) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          if (b < mb_active) {
+#pragma unroll
+            for (int c = 0; c < C::NPR; ++c) {
+              const u32x4 a0 = ld16(abase + b * 16 * APITCH + c * 128);
+              const u32x4 a1 = ld16(abase + b * 16 * APITCH + c * 128 + 64);
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m) {
+                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a0), bitcast<bf16x8>(bb[m][c].lo), acc[m][b]);
+                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a1), bitcast<bf16x8>(bb[m][c].hi), acc[m][b]);
+              }
+            }
+          }
+        }
+      } else {
+        float sb[NMAT][KB];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sb[m][kb] = bsc[m][ss * KB + kb];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          if (b < mb_active) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              u32x8 a;
+              a.lo = ld16(abase + b * 16 * APITCH + kb * 128);
+              a.hi = ld16(abase + b * 16 * APITCH + kb * 128 + 64);
+              float sa[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sa[i] = sAs[buf][(b * 16 + q * 4 + i) * KB + kb];
+#pragma unroll
+              for (int m = 0; m < NMAT; ++m) {
+                const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, bb[m][kb]),
+                    f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  acc[m][b][i] = fmaf(part[i], sa[i] * sb[m][kb], acc[m][b][i]);
+              }
+            }
+          }
+          // keep the partial sums of one row block live at a time
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+
+    // ---- pipeline: B one super-stage ahead in registers, A double-buffered in LDS
+    load_b(bq[0], 0);
+    load_a(0);
+    store_a(0);
+    __syncthreads();
+    auto step = [&](auto par, int ss) {
+      constexpr int P = decltype(par)::value;
+      if (ss + 1 < nss) {
+        load_b(bq[P ^ 1], ss + 1);
+        load_a(ss + 1);
+      }
+      compute(bq[P], ss & 1, ss);
+      if (ss + 1 < nss) store_a((ss + 1) & 1);
+      __syncthreads();
+    };
+    for (int ss = 0; ss < nss; ss += 2) {
+      step(std::integral_constant<int, 0>{}, ss);
+      if (ss + 1 < nss) step(std::integral_constant<int, 1>{}, ss + 1);
+    }
+
+    // ---- epilogue (A buffers are free: every wave passed the last barrier)
+    if constexpr (SWIGLU && C::FP8) {
+      float zv[MB][4];
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          zv[b][i] = silu_mul(acc[0][b][i], acc[1][b][i]);
+          const float mx = group16_max(fabsf(zv[b][i]));
+          if (r16 == 0) red[wave * BM + b * 16 + q * 4 + i] = mx;
+        }
+      __syncthreads();
+      // per-row scale; codes staged as [BM][128] bytes
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = b * 16 + q * 4 + i;
+          float amax = 0.0f;
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) amax = fmaxf(amax, red[w * BM + row]);
+          const float sc = e4m3_scale(amax);
+          lds[row * BN + wave * 16 + r16] = static_cast<uint8_t>(f32_to_e4m3(zv[b][i] / sc));
+          if (wave == 0 && r16 == 0 && row < rows)
+            p.c_scale[static_cast<int64_t>(tile.row0 + row) * p.c_scale_pitch + n0 / 128] = sc;
+        }
+      __syncthreads();
+      constexpr int PIECES = BM * BN / 16;
+      for (int c = tid; c < PIECES; c += THREADS) {
+        const int row = c / (BN / 16), col = c % (BN / 16);
+        if (row < rows)
+          st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 + col * 16,
+               ld16(lds + row * BN + col * 16));
+      }
+    } else {
+      uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = b * 16 + q * 4 + i;
+          const float v = SWIGLU ? silu_mul(acc[0][b][i], acc[NMAT - 1][b][i]) : acc[0][b][i];
+          o16[row * BN + wave * 16 + r16] = f32_to_bf16(v);
+        }
+      __syncthreads();
+      constexpr int PIECES = BM * BN * 2 / 16;
+      for (int c = tid; c < PIECES; c += THREADS) {
+        const int row = c / (BN * 2 / 16), col = c % (BN * 2 / 16);
+        if (row < rows)
+          st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
+               ld16(lds + row * BN * 2 + col * 16));
+      }
+    }
+    // the next item's first barrier orders these LDS reads before reuse
+  }
+}
+
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
+hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
+  auto kern = stream_gemm_kernel<EL, WAVES, BM, SS, SWIGLU>;
+  static int per_cu = -1, cus = 0;
+  if (per_cu < 0) {
+    int dev = 0;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void *>(kern), WAVES * 64, 0);
+    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+  }
+  constexpr int BN = 16 * WAVES;
+  const int nmax = a.N > a.Ns ? a.N : a.Ns;
+  const int64_t items = static_cast<int64_t>(a.tiles_ub) * (nmax / BN);
+  int64_t grid = static_cast<int64_t>(cus) * per_cu;
+  if (items < grid) grid = items;
+  if (grid <= 0) return hipSuccess;
+  kern<<<static_cast<unsigned>(grid), WAVES * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
+                              hipStream_t s) {
+  const bool gu = kind == GemmKind::GateUp;
+  if (elem == 1) {
+    if (bm == 64)
+      return gu ? launch_stream<Elem::BF16, 4, 64, 512, true>(a, s)
+                : launch_stream<Elem::BF16, 8, 64, 512, false>(a, s);
+    if (bm == 128)
+      return gu ? launch_stream<Elem::BF16, 4, 128, 256, true>(a, s)
+                : launch_stream<Elem::BF16, 8, 128, 256, false>(a, s);
+  } else if (elem == 2) {
+    if (bm == 64)
+      return gu ? launch_stream<Elem::FP8, 8, 64, 256, true>(a, s)
+                : launch_stream<Elem::FP8, 8, 64, 256, false>(a, s);
+    if (bm == 128)
+      return gu ? launch_stream<Elem::FP8, 8, 128, 256, true>(a, s)
+                : launch_stream<Elem::FP8, 8, 128, 256, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace afd

@@ -27,10 +27,12 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
 
 // Histogram, scan and stable scatter of the (token, slot) pairs; GEMM tile
 // list for row tiles of `bm` rows (routed experts, then S shared groups).
+// Also zeroes `counters[0..ncounters)` (the GEMMs' work counters).
 hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
                            int bm, int32_t *counts, int32_t *offsets,
                            int32_t *perm, int32_t *slot_row, Tile *tiles,
-                           int32_t *num_tiles, hipStream_t s);
+                           int32_t *num_tiles, int32_t *counters,
+                           int ncounters, hipStream_t s);
 
 hipError_t launch_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
                               uint8_t *q, float *sc, hipStream_t s);
@@ -59,6 +61,7 @@ struct GemmArgs {
   int E;
   const Tile *tiles;
   const int32_t *num_tiles;
+  int32_t *work_counter;  // persistent kernels: next work item (starts at 0)
   int tiles_ub;          // upper bound of the tile count (grid sizing)
   // C: output rows indexed by dispatched row, pitch c_pitch bytes.
   uint8_t *C;
@@ -67,12 +70,20 @@ struct GemmArgs {
   int c_scale_pitch;
 };
 
-// Tile height (rows per tile) the GEMMs of a mode use for T tokens; the
-// dispatch kernel builds the tile list with the same value.
-int gemm_bm(int elem, int T, int k, int E);
+// GEMM variant for a forward: row tile height (the dispatch kernel builds
+// the tile list with it) and whether the weight-streaming kernel is used.
+struct GemmPlan {
+  int bm;
+  bool stream;
+};
+GemmPlan gemm_plan(int elem, int T, int k, int E);
 
+// LDS-tiled kernel (all element types).
 hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,
                        hipStream_t s);
+// Weight-streaming persistent kernel (bf16, fp8; bm 64 or 128).
+hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
+                              hipStream_t s);
 
 // out[t] = sum_j w[t,j] Y[slot_row[t,j]] + sum_s Y[Tk + s*T + t].
 hipError_t launch_combine(bool f32, const uint8_t *Y, const int32_t *slot_row,

@@ -73,6 +73,8 @@ SMALL = [
     LayerShape("f32_k_eq_e", T=70, h=128, E=4, k=4, I=128, S=1, Is=256, mode="f32"),
     LayerShape("w8a8_small", T=200, h=512, E=8, k=2, I=256, S=1, Is=384, mode="w8a8"),
     LayerShape("w8a8_many", T=96, h=256, E=32, k=8, I=384, mode="w8a8"),
+    LayerShape("w8a8_dense", T=600, h=256, E=8, k=2, I=256, S=1, Is=128, mode="w8a8"),
+    LayerShape("bf16_dense", T=700, h=256, E=4, k=1, I=128, S=1, Is=384, mode="bf16"),
 ]
 
 
