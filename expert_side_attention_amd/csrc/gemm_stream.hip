@@ -107,8 +107,14 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
     __syncthreads();
 
     const int ES = C::FP8 ? 1 : 2;
-    const int64_t krow = static_cast<int64_t>(K) * ES;
-    const int nss = static_cast<int>(krow / SS);
+    const int64_t krow = static_cast<int64_t>(K) * ES;  // a multiple of 128
+    // the last super-stage may be partial: it holds `valid_pairs` 128-byte
+    // K pieces; nothing beyond a row's end is ever read
+    const int nss = static_cast<int>((krow + SS - 1) / SS);
+    auto valid_pairs = [&](int ss) {
+      const int64_t left = (krow - static_cast<int64_t>(ss) * SS) / 128;
+      return left < C::NPR ? static_cast<int>(left) : C::NPR;
+    };
     const int64_t mat = static_cast<int64_t>(N) * krow;
     const uint8_t *bptr[NMAT];
     {
@@ -134,23 +140,29 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
     u32x4 ra[RA];
     float as_reg = 0.0f;
     auto load_b = [&](u32x8 (&dst)[NMAT][C::NPR], int ss) {
+      const int vp = valid_pairs(ss);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int c = 0; c < C::NPR; ++c) {
-          const uint8_t *src = bptr[m] + static_cast<int64_t>(ss) * SS + c * 128;
-          dst[m][c].lo = ld16(src);
-          dst[m][c].hi = ld16(src + 64);
+          if (c < vp) {
+            const uint8_t *src = bptr[m] + static_cast<int64_t>(ss) * SS + c * 128;
+            dst[m][c].lo = ld16(src);
+            dst[m][c].hi = ld16(src + 64);
+          } else {
+            dst[m][c] = u32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          }
         }
     };
     auto load_a = [&](int ss) {
+      const int vcols = valid_pairs(ss) * 8;  // valid 16-byte columns
 #pragma unroll
       for (int i = 0; i < RA; ++i) {
         const int c = tid + THREADS * i;
         if (c < ACH) {
           const int row = c / (SS / 16), col = c % (SS / 16);
           const int src = rowsrc[row];
-          if (src >= 0)
+          if (src >= 0 && col < vcols)
             ra[i] = ld16(p.A + src * p.a_pitch + static_cast<int64_t>(ss) * SS + col * 16);
           else
             ra[i] = u32x4{0, 0, 0, 0};
@@ -159,8 +171,9 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
       if constexpr (C::FP8) {
         if (tid < BM * KB) {
           const int src = rowsrc[tid / KB];
-          as_reg = src >= 0 ? p.a_scale[static_cast<int64_t>(src) * p.a_scale_pitch + ss * KB + tid % KB]
-                            : 0.0f;
+          as_reg = (src >= 0 && tid % KB < valid_pairs(ss))
+                       ? p.a_scale[static_cast<int64_t>(src) * p.a_scale_pitch + ss * KB + tid % KB]
+                       : 0.0f;
         }
       }
     };
@@ -185,18 +198,21 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
 
     auto compute = [&](const u32x8 (&bb)[NMAT][C::NPR], int buf, int ss) {
       const uint8_t *abase = lds + buf * BM * APITCH + r16 * APITCH + q * 16;
+      const int vp = valid_pairs(ss);
       if constexpr (!C::FP8) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
           if (b < mb_active) {
 #pragma unroll
             for (int c = 0; c < C::NPR; ++c) {
-              const u32x4 a0 = ld16(abase + b * 16 * APITCH + c * 128);
-              const u32x4 a1 = ld16(abase + b * 16 * APITCH + c * 128 + 64);
+              if (c < vp) {
+                const u32x4 a0 = ld16(abase + b * 16 * APITCH + c * 128);
+                const u32x4 a1 = ld16(abase + b * 16 * APITCH + c * 128 + 64);
 #pragma unroll
-              for (int m = 0; m < NMAT; ++m) {
-                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a0), bitcast<bf16x8>(bb[m][c].lo), acc[m][b]);
-                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a1), bitcast<bf16x8>(bb[m][c].hi), acc[m][b]);
+                for (int m = 0; m < NMAT; ++m) {
+                  acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a0), bitcast<bf16x8>(bb[m][c].lo), acc[m][b]);
+                  acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a1), bitcast<bf16x8>(bb[m][c].hi), acc[m][b]);
+                }
               }
             }
           }
@@ -206,12 +222,13 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) sb[m][kb] = bsc[m][ss * KB + kb];
+          for (int kb = 0; kb < KB; ++kb) sb[m][kb] = kb < vp ? bsc[m][ss * KB + kb] : 0.0f;
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
           if (b < mb_active) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
+              if (kb >= vp) continue;
               u32x8 a;
               a.lo = ld16(abase + b * 16 * APITCH + kb * 128);
               a.hi = ld16(abase + b * 16 * APITCH + kb * 128 + 64);
