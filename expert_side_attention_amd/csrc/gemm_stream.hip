@@ -259,9 +259,12 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
     __syncthreads();
     auto step = [&](auto par, int ss) {
       constexpr int P = decltype(par)::value;
+      // activation rows first: the LDS store at the end of this step waits
+      // for them, and vector loads complete in issue order, so the weight
+      // loads issued after them stay in flight across the barrier
       if (ss + 1 < nss) {
-        load_b(bq[P ^ 1], ss + 1);
         load_a(ss + 1);
+        load_b(bq[P ^ 1], ss + 1);
       }
       compute(bq[P], ss & 1, ss);
       if (ss + 1 < nss) store_a((ss + 1) & 1);

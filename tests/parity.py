@@ -60,6 +60,20 @@ def check_routing(logits, beta, gpu_ids, k):
     return np.any(g != oracle_ids, axis=1)
 
 
+def check_weights(gpu_w, ref_w, beta, gpu_ids, same):
+    """Routing weights: with logit errors |d_i| <= beta_i, log w_j moves by at
+    most 2 max_i beta_i, so |dw_j| <= w_j (exp(2 max beta) - 1) (+ fp32 rounding of the
+    exp/sum/divide, at most about (k + 3) 2^-24 relative, covered by 1e-6)."""
+    g = np.asarray(gpu_w, np.float64)[same]
+    r = np.asarray(ref_w, np.float64)[same]
+    bmax = np.take_along_axis(beta, np.asarray(gpu_ids, np.int64), 1)[same].max(axis=1,
+                                                                                   keepdims=True)
+    bound = r * np.expm1(2 * bmax) + 1e-6
+    err = np.abs(g - r)
+    assert np.all(err <= bound), f"weights off by {err.max():.3e} (max err/bound {np.max(err / bound):.2f})"
+    return float(np.max(err / bound)) if err.size else 0.0
+
+
 def check_dispatch(gpu_tr, E):
     ids = gpu_tr["topk_ids"]
     counts, offsets, perm, slot_row = O.dispatch(ids, E)

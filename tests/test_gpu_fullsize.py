@@ -13,7 +13,8 @@ import torch
 from afd_inputs import CONFIGS, SyntheticLayer
 from oracle import afd_oracle as O
 
-from parity import check_dispatch, check_outputs, check_routing, decode_store, routing_slack
+from parity import (check_dispatch, check_outputs, check_routing, check_weights, decode_store,
+                    routing_slack)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -71,7 +72,8 @@ def check_full(name, microbatches=1, n_sample=12):
     assert differ.mean() <= 0.01
     same = ~differ
     gpu_w = np.concatenate([tr["topk_w"] for tr in trs])
-    assert np.allclose(gpu_w[same], w[same], rtol=0, atol=2e-6)
+    ratio = check_weights(gpu_w, w, beta, gpu_ids, same)
+    print(f"[fullsize] {name}: routing weights within {ratio:.2f} of their bound", flush=True)
     for tr in trs:
         check_dispatch(tr, s.E)
     if s.mode == "w8a8":

@@ -9,8 +9,8 @@ import torch
 from afd_inputs import CONFIGS, LayerShape, SyntheticLayer, f32_to_bf16_bits, tie_case
 from oracle import afd_oracle as O
 
-from parity import (TOL, check_dispatch, check_outputs, check_routing, decode_store,
-                    routing_slack)
+from parity import (TOL, check_dispatch, check_outputs, check_routing, check_weights,
+                    decode_store, routing_slack)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False):
     assert differ.mean() <= 0.01, f"{differ.sum()} tokens route differently"
     check_dispatch(tr, s.E)
     same = ~differ
-    assert np.allclose(tr["topk_w"][same], ref["w"][same], rtol=0, atol=2e-6)
+    check_weights(tr["topk_w"], ref["w"], beta, tr["topk_ids"], same)
     if s.mode == "w8a8":
         assert np.array_equal(tr["x_q"], ref["x_q"])
         assert np.array_equal(tr["x_s"], ref["x_s"])
