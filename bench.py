@@ -70,6 +70,24 @@ def work_model(s, counts):
     }
 
 
+def work_model_microbatches(s, layers, xs):
+    """Sum of the per-micro-batch models: each micro-batch streams the
+    weights of the experts it touches."""
+    tot = None
+    for li, xi in zip(layers, xs):
+        _, tr = li.forward(xi, trace=True)
+        import torch
+        torch.cuda.synchronize()
+        m = work_model(s.with_tokens(xi.shape[0]), tr["counts"].cpu().tolist())
+        if tot is None:
+            tot = dict(m)
+        else:
+            for kk in ("gate_up_bytes", "gate_up_flops", "forward_bytes", "forward_flops"):
+                tot[kk] += m[kk]
+            tot["touched_experts"] = max(tot["touched_experts"], m["touched_experts"])
+    return tot
+
+
 def cpu_baseline(syn, min_seconds=10.0):
     """The fp64 oracle on the same batch, weights pre-drawn in host memory."""
     import numpy as np
@@ -137,48 +155,82 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     shape = CONFIGS[args.workload]
-    if shape.micro_batches != 1:
-        raise SystemExit("two-stream workloads are timed by their own script")
     syn = SyntheticLayer(shape, seed=args.seed)
     dev = "cuda:0"
     log(f"[bench] building {shape.name} on {dev}")
-    layer = build_layer(syn, dev)
+    nmb = shape.micro_batches
+    mbT = shape.T // nmb
+    layer = build_layer(syn, dev, max_tokens=mbT)
+    layers = [layer] + [layer.sibling() for _ in range(nmb - 1)]
     x = hidden_tensor(syn, dev)
-    out = torch.empty_like(x)
-    _, tr = layer.forward(x, trace=True)
-    torch.cuda.synchronize()
-    counts = tr["counts"].cpu().tolist()
-    model = work_model(shape, counts)
+    xs = [x[i * mbT:(i + 1) * mbT] for i in range(nmb)]
+    outs = [torch.empty_like(xi) for xi in xs]
+    # weights touched per micro-batch (each micro-batch streams its own)
+    model = work_model_microbatches(shape, layers, xs)
+    streams = ([torch.cuda.current_stream()] if nmb == 1
+               else [torch.cuda.Stream() for _ in range(nmb)])
 
-    stream = torch.cuda.current_stream()
+    def step():
+        for li, xi, oi, st in zip(layers, xs, outs, streams):
+            li.forward(xi, out=oi, stream=st)
+
     for _ in range(args.warmup):
-        layer.forward(x, out=out, stream=stream)
+        step()
     torch.cuda.synchronize()
-    layer.profile_read()  # reset
+    for li in layers:
+        li.profile_read()  # reset
 
-    # timed region: K steps; HIP events around the gate/up GEMM launches
-    layer.profile_enable(["gate_up"])
+    # timed region: K steps; HIP events around the gate/up GEMM launches,
+    # recorded on the stream each forward runs on
+    for li in layers:
+        li.profile_enable(["gate_up"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        layer.forward(x, out=out, stream=stream)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prof = layer.profile_read()
-    layer.profile_enable([])
+    gu_ms = gu_n = 0
+    for li in layers:
+        prof = li.profile_read()
+        li.profile_enable([])
+        gu_ms += prof["gate_up"][0]
+        gu_n += prof["gate_up"][1]
     ms_step = (t1 - t0) * 1e3 / args.steps
-    gu_ms, gu_n = prof["gate_up"]
     gu_avg = gu_ms / max(gu_n, 1)
 
-    # untimed breakdown of all stages
-    layer.profile_enable(["router", "dispatch", "quant", "gate_up", "down", "combine"])
+    # untimed breakdown of all stages, one micro-batch at a time
+    all_stages = ["router", "dispatch", "quant", "gate_up", "down", "combine"]
+    stage_tot = {}
+    for li in layers:
+        li.profile_enable(all_stages)
     for _ in range(10):
-        layer.forward(x, out=out, stream=stream)
+        for li, xi, oi in zip(layers, xs, outs):
+            li.forward(xi, out=oi)
     torch.cuda.synchronize()
-    stages = {k: round(v[0] / v[1], 4) for k, v in layer.profile_read().items() if v[1]}
-    layer.profile_enable([])
+    for li in layers:
+        for kk, v in li.profile_read().items():
+            if v[1]:
+                a = stage_tot.setdefault(kk, [0.0, 0])
+                a[0] += v[0]
+                a[1] += v[1]
+        li.profile_enable([])
+    stages = {kk: round(v[0] / v[1], 4) for kk, v in stage_tot.items()}
+    # serial time of one step (micro-batches back to back on one stream)
+    torch.cuda.synchronize()
+    ts0 = time.perf_counter()
+    for _ in range(max(1, args.steps // 4)):
+        for li, xi, oi in zip(layers, xs, outs):
+            li.forward(xi, out=oi)
+    torch.cuda.synchronize()
+    ms_serial = (time.perf_counter() - ts0) * 1e3 / max(1, args.steps // 4)
 
-    achieved = model["gate_up_bytes"] / (gu_avg * 1e-3) / 1e9
+    ai = model["forward_flops"] / model["forward_bytes"]
+    ridge = MFMA_PEAK_TFLOPS[shape.mode] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if ai > ridge else "hbm"
+    gu_launch_bytes = model["gate_up_bytes"] / nmb
+    gu_launch_flops = model["gate_up_flops"] / nmb
+    achieved = gu_launch_bytes / (gu_avg * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{shape.name}.json")
     if os.path.exists(tfile):
@@ -204,15 +256,26 @@ def main():
         "config": {"workload": shape.name, "T": shape.T, "h": shape.h, "E": shape.E,
                    "k": shape.k, "I": shape.I, "S": shape.S, "Is": shape.Is,
                    "mode": shape.mode, "seed": args.seed},
-        "roofline": {"bound": "hbm", "kernel": "gate_up grouped GEMM + SwiGLU",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(gu_avg, 5),
-                     "algorithmic_bytes_per_launch": int(model["gate_up_bytes"])},
+        "roofline": ({"bound": "hbm", "kernel": "gate_up grouped GEMM + SwiGLU",
+                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                      "avg_launch_ms": round(gu_avg, 5),
+                      "algorithmic_bytes_per_launch": int(gu_launch_bytes)}
+                     if bound == "hbm" else
+                     {"bound": "mfma", "kernel": "gate_up grouped GEMM + SwiGLU",
+                      "achieved": round(gu_launch_flops / (gu_avg * 1e-3) / 1e12, 2),
+                      "peak": MFMA_PEAK_TFLOPS[shape.mode], "unit": "TFLOP/s",
+                      "frac": round(gu_launch_flops / (gu_avg * 1e-3) / 1e12
+                                    / MFMA_PEAK_TFLOPS[shape.mode], 4),
+                      "traffic": traffic, "avg_launch_ms": round(gu_avg, 5),
+                      "algorithmic_flops_per_launch": int(gu_launch_flops)}),
         "forward": {"hbm_gbs": round(fwd_gbs, 1), "hbm_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
                     "bytes": int(model["forward_bytes"]),
                     "tflops": round(model["forward_flops"] / (ms_step * 1e-3) / 1e12, 2),
+                    "mfma_frac": round(model["forward_flops"] / (ms_step * 1e-3) / 1e12
+                                       / MFMA_PEAK_TFLOPS[shape.mode], 4),
                     "touched_experts": model["touched_experts"],
+                    "micro_batches": nmb, "ms_serial_one_stream": round(ms_serial, 5),
                     "stage_ms": stages},
         "cpu_baseline": None,
     }

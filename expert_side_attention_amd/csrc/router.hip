@@ -9,10 +9,11 @@
 // "一个在啃带宽，一个在吃算力"); the softmax, the tie rule and the
 // renormalisation are this library's reading of that step.
 //
-// bf16 path: X rows are staged through LDS (shared by the 4 waves), router
-// rows stream from global/L2 straight into MFMA operand registers (each
-// wave owns a disjoint set of 16-expert column blocks, so no LDS sharing is
-// needed for them).  fp32 path (small layers): one dot product per thread.
+// bf16 path (E <= 256): split-K over the 4 waves, operands straight from
+// global memory into MFMA registers, partial logits summed in wave order.
+// bf16 path (E <= 512): X rows staged through LDS, each wave owning a set of
+// 16-expert column blocks.  fp32 path (small layers): one dot product per
+// thread.
 #include "common.h"
 #include "kernels.h"
 
@@ -193,6 +194,116 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   topk_from_lds<TM, NC>(sl, selv, t0, T, E, k, ids, wout);
 }
 
+// bf16 router, split-K: the 4 waves of a workgroup take disjoint quarters of
+// h and each computes all TM x E partial logits straight from global memory
+// (no LDS, no barrier in the K loop; operands prefetched NBUF chunks ahead),
+// then the four partial sums are added in wave order through LDS, so the
+// result does not depend on timing.  NB = 16-expert column blocks (E <= 16 NB).
+template <int TM, int NB, int NBUF>
+__global__ __launch_bounds__(256) void router_bf16_splitk_kernel(
+    const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wr,
+    const float *__restrict__ bias, int T, int h, int E, int k,
+    int32_t *__restrict__ ids, float *__restrict__ wout) {
+  constexpr int MB = TM / 16;
+  constexpr int NC = (NB * 16 + 63) / 64;
+  __shared__ float red[4 * TM * NB * 16];
+  __shared__ float selv[4 * kMaxExperts];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int t0 = blockIdx.x * TM;
+  const int kq = h / 4;            // this wave's K range: [wave * kq, wave * kq + kq)
+  const int nchunks = kq / 32;     // 32 K elements per MFMA
+  const int kbase = wave * kq + q * 8;
+
+  const uint16_t *arow[MB];
+  bool avalid[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int t = t0 + m * 16 + r16;
+    avalid[m] = t < T;
+    arow[m] = X + static_cast<int64_t>(avalid[m] ? t : 0) * h + kbase;
+  }
+  const uint16_t *brow[NB];
+  bool bvalid[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int e = n * 16 + r16;
+    bvalid[n] = e < E;
+    brow[n] = Wr + static_cast<int64_t>(bvalid[n] ? e : 0) * h + kbase;
+  }
+
+  u32x4 fa[NBUF][MB], fb[NBUF][NB];
+  auto load = [&](int buf, int c) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      fa[buf][m] = avalid[m] ? ld16(arow[m] + c * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      fb[buf][n] = bvalid[n] ? ld16(brow[n] + c * 32) : u32x4{0, 0, 0, 0};
+  };
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
+
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b)
+    if (b < nchunks) load(b, b);
+  for (int c0 = 0; c0 < nchunks; c0 += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int c = c0 + b;
+      if (c < nchunks) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int n = 0; n < NB; ++n)
+            acc[m][n] = mfma_bf16_k32(bitcast<bf16x8>(fa[b][m]), bitcast<bf16x8>(fb[b][n]),
+                                      acc[m][n]);
+        if (c + NBUF < nchunks) load(b, c + NBUF);
+      }
+    }
+  }
+
+  // partial logits -> LDS, then a fixed-order sum over the 4 waves
+  constexpr int EP = NB * 16;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(wave * TM + m * 16 + q * 4 + i) * EP + n * 16 + r16] = acc[m][n][i];
+  __syncthreads();
+  // sums into registers first, then (after a barrier) compacted to pitch E
+  constexpr int PER = (TM * EP + 255) / 256;
+  float sum[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + 256 * j;
+    sum[j] = 0.0f;
+    if (i < TM * E) {
+      const int tt = i / E, e = i % E;
+      float v = red[tt * EP + e];
+      v += red[(TM + tt) * EP + e];
+      v += red[(2 * TM + tt) * EP + e];
+      v += red[(3 * TM + tt) * EP + e];
+      if (bias) v += bias[e];
+      sum[j] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + 256 * j;
+    if (i < TM * E) red[i] = sum[j];
+  }
+  __syncthreads();
+  topk_from_lds<TM, NC>(red, selv, t0, T, E, k, ids, wout);
+}
+
 // fp32 router for small layers: one (token, expert) dot product per thread.
 template <int TM>
 __global__ __launch_bounds__(256) void router_f32_kernel(
@@ -232,16 +343,15 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   const uint16_t *X = static_cast<const uint16_t *>(x);
   const uint16_t *W = static_cast<const uint16_t *>(wr);
   if (E <= 64) {
-    // one 16-expert block per wave
-    if (T <= 2048)
-      router_bf16_kernel<16, 1><<<(T + 15) / 16, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
+    if (T <= 4096)
+      router_bf16_splitk_kernel<16, 4, 4><<<(T + 15) / 16, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
     else
-      router_bf16_kernel<64, 1><<<(T + 63) / 64, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
+      router_bf16_splitk_kernel<32, 4, 2><<<(T + 31) / 32, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
   } else if (E <= 256) {
-    if (T <= 2048)
-      router_bf16_kernel<16, 4><<<(T + 15) / 16, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
+    if (T <= 4096)
+      router_bf16_splitk_kernel<16, 16, 2><<<(T + 15) / 16, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
     else
-      router_bf16_kernel<64, 4><<<(T + 63) / 64, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
+      router_bf16_splitk_kernel<32, 16, 1><<<(T + 31) / 32, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
   } else {
     router_bf16_kernel<32, 8><<<(T + 31) / 32, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
   }

@@ -102,6 +102,7 @@ class FfnLayer:
                       sh_gate_w, sh_up_w, sh_down_w, sh_gate_s, sh_up_s, sh_down_s]
         self.device = dev
         self.hidden, self.num_experts, self.top_k = h, E, top_k
+        self.inter, self.shared_inter = I, Is
         self.num_shared, self.max_tokens = S, max_tokens
         self.act_dtype = act
         cfg = F.afd_ffn_config(
@@ -111,6 +112,17 @@ class FfnLayer:
         w = F.afd_ffn_weights(*[_ptr(t) for t in self._keep])
         with torch.cuda.device(dev):
             self._h = F.afd_ffn_create(cfg, w)
+
+    def sibling(self) -> "FfnLayer":
+        """Another handle (own workspace) over the same weights, for a second
+        micro-batch on another stream."""
+        k = self._keep
+        return FfnLayer(mode=self.mode, hidden=self.hidden, num_experts=self.num_experts,
+                        top_k=self.top_k, inter=self.inter, max_tokens=self.max_tokens,
+                        router_w=k[0], router_b=k[1], gate_w=k[2], up_w=k[3], down_w=k[4],
+                        gate_s=k[5], up_s=k[6], down_s=k[7], num_shared=self.num_shared,
+                        shared_inter=self.shared_inter, sh_gate_w=k[8], sh_up_w=k[9],
+                        sh_down_w=k[10], sh_gate_s=k[11], sh_up_s=k[12], sh_down_s=k[13])
 
     def forward(self, hidden: torch.Tensor, out: torch.Tensor = None, stream=None,
                 trace: bool = False):
