@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libafd_ffn.so")
 
 SOURCES = ["router.hip", "dispatch.hip", "quant.hip", "gemm.hip",
-           "gemm_stream.hip", "combine.hip", "api.cpp"]
+           "gemm_stream.hip", "gemm_prefill.hip", "combine.hip", "api.cpp"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are switched off for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -56,7 +56,8 @@ struct afd_ffn_handle {
   void *ws;
   size_t ws_bytes;
   int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *counters;
-  float *topk_w;
+  int32_t *router_counters;
+  float *topk_w, *logits;
   afd::Tile *tiles;
   uint8_t *xq;
   float *xs;
@@ -189,6 +190,8 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
       {reinterpret_cast<void **>(&h->offsets), sizeof(int32_t) * (E + 1)},
       {reinterpret_cast<void **>(&h->num_tiles), sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->counters), 2 * sizeof(int32_t)},
+      {reinterpret_cast<void **>(&h->router_counters), sizeof(int32_t) * afd::router_blocks(T)},
+      {reinterpret_cast<void **>(&h->logits), sizeof(float) * T * E},
       {reinterpret_cast<void **>(&h->tiles), sizeof(afd::Tile) * h->tiles_cap},
       {reinterpret_cast<void **>(&h->z), static_cast<size_t>(R) * h->zpitch * zes},
       {reinterpret_cast<void **>(&h->y), static_cast<size_t>(R) * hd * yes},
@@ -214,6 +217,15 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
     *p.dst = static_cast<char *>(h->ws) + off;
     off += align_up(p.bytes, 256);
   }
+  // the router's completion counters start at zero; every forward leaves
+  // them at zero again
+  e = hipMemset(h->router_counters, 0, sizeof(int32_t) * afd::router_blocks(T));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    hipFree(h->ws);
+    delete h;
+    return hip_fail(e, "workspace initialisation");
+  }
   *out = h;
   return AFD_OK;
 }
@@ -231,6 +243,18 @@ void afd_ffn_destroy(afd_ffn_handle *h) {
   hipFree(h->ws);
   hipSetDevice(cur);
   delete h;
+}
+
+static hipError_t launch_gemms(afd::GemmKind kind, const afd::GemmPlan &plan, int elem,
+                               const afd::GemmArgs &a, hipStream_t s) {
+  switch (plan.kernel) {
+    case afd::GemmKernel::Stream:
+      return afd::launch_gemm_stream(kind, elem, plan.bm, a, s);
+    case afd::GemmKernel::Prefill:
+      return afd::launch_gemm_prefill(kind, a, s);
+    default:
+      return afd::launch_gemm(kind, elem, plan.bm, a, s);
+  }
 }
 
 static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
@@ -263,8 +287,8 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
 
   ev = prof_begin(h, AFD_STAGE_ROUTER, s);
   e = afd::launch_router(h->elem == 0, hidden, h->w.router_w,
-                         c.has_router_bias ? h->w.router_b : nullptr, Ti, hd, E, k, h->ids,
-                         h->topk_w, s);
+                         c.has_router_bias ? h->w.router_b : nullptr, Ti, hd, E, k, h->logits,
+                         h->router_counters, h->ids, h->topk_w, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
 
@@ -318,8 +342,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   g.c_scale = h->zs;
   g.c_scale_pitch = h->zpitch / 128;
   ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
-  e = plan.stream ? afd::launch_gemm_stream(afd::GemmKind::GateUp, h->elem, plan.bm, g, s)
-                  : afd::launch_gemm(afd::GemmKind::GateUp, h->elem, plan.bm, g, s);
+  e = launch_gemms(afd::GemmKind::GateUp, plan, h->elem, g, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
 
@@ -346,8 +369,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   d.c_scale = nullptr;
   d.work_counter = h->counters + 1;
   ev = prof_begin(h, AFD_STAGE_DOWN, s);
-  e = plan.stream ? afd::launch_gemm_stream(afd::GemmKind::Down, h->elem, plan.bm, d, s)
-                  : afd::launch_gemm(afd::GemmKind::Down, h->elem, plan.bm, d, s);
+  e = launch_gemms(afd::GemmKind::Down, plan, h->elem, d, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
 

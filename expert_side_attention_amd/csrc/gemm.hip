@@ -296,13 +296,15 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 GemmPlan gemm_plan(int elem, int T, int k, int E) {
-  if (elem == 0) return {32, false};
+  if (elem == 0) return {32, GemmKernel::Tiled};
   // rows per expert on average decide the regime: a few dozen rows per
-  // expert -> stream the weights once with a tile that holds all of them
+  // expert -> stream the weights once with a tile that holds all of them;
+  // hundreds of rows -> compute-bound 256-row tiles (bf16)
   const int64_t avg = (static_cast<int64_t>(T) * k + E - 1) / E;
-  if (avg <= 48) return {64, true};
-  if (avg <= 112) return {128, true};
-  return {64, false};
+  if (avg <= 48) return {64, GemmKernel::Stream};
+  if (avg <= 112) return {128, GemmKernel::Stream};
+  if (elem == 1) return {256, GemmKernel::Prefill};
+  return {64, GemmKernel::Tiled};
 }
 
 hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,

@@ -20,10 +20,14 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxShared = 8;
 
 // Router GEMM + softmax + top-k + renormalisation.
-// f32: x, wr are fp32; else bf16.  bias may be null.
+// f32: x, wr are fp32; else bf16.  bias may be null.  bf16 path scratch:
+// logits [T, E] fp32 and counters [router_blocks(T)] int32, which must be
+// zero before the first call and are left zero by every call.
+int router_blocks(int T);
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
-                         int32_t *ids, float *w, hipStream_t s);
+                         float *logits, int32_t *counters, int32_t *ids, float *w,
+                         hipStream_t s);
 
 // Histogram, scan and stable scatter of the (token, slot) pairs; GEMM tile
 // list for row tiles of `bm` rows (routed experts, then S shared groups).
@@ -71,10 +75,11 @@ struct GemmArgs {
 };
 
 // GEMM variant for a forward: row tile height (the dispatch kernel builds
-// the tile list with it) and whether the weight-streaming kernel is used.
+// the tile list with it) and which kernel family runs the two GEMMs.
+enum class GemmKernel { Tiled = 0, Stream = 1, Prefill = 2 };
 struct GemmPlan {
   int bm;
-  bool stream;
+  GemmKernel kernel;
 };
 GemmPlan gemm_plan(int elem, int T, int k, int E);
 
@@ -84,6 +89,8 @@ hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,
 // Weight-streaming persistent kernel (bf16, fp8; bm 64 or 128).
 hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
                               hipStream_t s);
+// Compute-bound kernel (bf16, bm 256).
+hipError_t launch_gemm_prefill(GemmKind kind, const GemmArgs &a, hipStream_t s);
 
 // out[t] = sum_j w[t,j] Y[slot_row[t,j]] + sum_s Y[Tk + s*T + t].
 hipError_t launch_combine(bool f32, const uint8_t *Y, const int32_t *slot_row,

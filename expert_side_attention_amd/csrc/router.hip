@@ -1,7 +1,6 @@
 // Router: logits = X W_r^T (+ b), then top-k with ties to the lower expert
 // index, then the softmax restricted to the selected experts and
-// renormalised.  One workgroup owns TM tokens and all E experts, so the
-// whole routing decision of a token stays on chip.
+// renormalised.
 //
 // The pages name routing as one of the two costs of the expert path (vLLM
 // AFD plugin page, "Attention-FFN 解耦的原理") and experts as sparsely
@@ -9,18 +8,13 @@
 // "一个在啃带宽，一个在吃算力"); the softmax, the tie rule and the
 // renormalisation are this library's reading of that step.
 //
-// bf16 path (E <= 256): split-K over the 4 waves, operands straight from
-// global memory into MFMA registers, partial logits summed in wave order.
-// bf16 path (E <= 512): X rows staged through LDS, each wave owning a set of
-// 16-expert column blocks.  fp32 path (small layers): one dot product per
-// thread.
+// bf16 path: see router_bf16_kernel.  fp32 path (small layers): one dot
+// product per thread, one workgroup per 16 tokens.
 #include "common.h"
 #include "kernels.h"
 
 namespace afd {
 namespace {
-
-constexpr int kRowB = 144;  // LDS pitch of a 128-byte K stage row (+16 pad)
 
 // Sortable key: larger logit first, then smaller index.  Key 0 = removed.
 __device__ __forceinline__ unsigned long long topk_key(float v, int e) {
@@ -87,133 +81,33 @@ __device__ void topk_from_lds(const float *sl, float *selv, int t0, int T,
   }
 }
 
-// bf16 router.  TM tokens per workgroup, NBPW 16-expert blocks per wave.
-template <int TM, int NBPW>
+// bf16 router.  The grid is (expert slices of EN) x (token blocks of TM), so
+// even small batches spread over many CUs.  Inside a workgroup the 4 waves
+// take disjoint quarters of h and compute all TM x EN partial logits with
+// operands loaded straight from global memory into MFMA registers (no LDS,
+// no barrier in the K loop, NBUF chunks of prefetch); the partial sums are
+// added in wave order, so the logits do not depend on timing.  Each
+// workgroup stores its logit slice; the last one to finish a token block
+// (device-scope counter) runs the top-k for that block and resets the
+// counter to 0 for the next call.
+template <int TM, int EN, int NBUF>
 __global__ __launch_bounds__(256) void router_bf16_kernel(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wr,
     const float *__restrict__ bias, int T, int h, int E, int k,
+    float *__restrict__ logits, int32_t *__restrict__ counters,
     int32_t *__restrict__ ids, float *__restrict__ wout) {
-  constexpr int MB = TM / 16;
-  constexpr int NC = (NBPW * 4 * 16) / 64;  // candidates per lane
-  __shared__ __align__(16) uint8_t smem[(2 * TM * kRowB > TM * NBPW * 64 * 4)
-                                            ? 2 * TM * kRowB
-                                            : TM * NBPW * 64 * 4];
+  constexpr int MB = TM / 16, NB = EN / 16;
+  constexpr int RED = 4 * TM * EN;
+  constexpr int TOPK = TM * kMaxExperts;
+  __shared__ float red[RED > TOPK ? RED : TOPK];
   __shared__ float selv[4 * kMaxExperts];
+  __shared__ int is_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, r16 = lane & 15;
-  const int t0 = blockIdx.x * TM;
-  const int nstages = h / 64;  // 64 bf16 = 128 bytes per stage
-
-  // A (X rows) staging: TM rows x 8 chunks of 16 bytes.
-  constexpr int ACH = TM * 8;
-  u32x4 ra[(ACH + 255) / 256];
-  auto load_a = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < (ACH + 255) / 256; ++i) {
-      const int c = tid + 256 * i;
-      if (c < ACH) {
-        const int row = c >> 3, col = c & 7;
-        const int t = t0 + row;
-        ra[i] = (t < T) ? ld16(X + static_cast<int64_t>(t) * h + s * 64 + col * 8)
-                        : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < (ACH + 255) / 256; ++i) {
-      const int c = tid + 256 * i;
-      if (c < ACH) st16(smem + buf * TM * kRowB + (c >> 3) * kRowB + (c & 7) * 16, ra[i]);
-    }
-  };
-  // B (router rows) straight to registers: block nb of this wave, row
-  // nb*16 + r16, bytes [32q, 32q + 32) of the stage.
-  Frag32 rb[NBPW];
-  auto load_b = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < NBPW; ++j) {
-      const int e = (wave + 4 * j) * 16 + r16;
-      if (e < E) {
-        const uint16_t *p = Wr + static_cast<int64_t>(e) * h + s * 64 + q * 16;
-        rb[j].lo = ld16(p);
-        rb[j].hi = ld16(p + 8);
-      } else {
-        rb[j].lo = u32x4{0, 0, 0, 0};
-        rb[j].hi = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-
-  f32x4 acc[MB][NBPW];
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int j = 0; j < NBPW; ++j) acc[m][j] = f32x4{0, 0, 0, 0};
-
-  load_a(0);
-  store_a(0);
-  load_b(0);
-  __syncthreads();
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    Frag32 cb[NBPW];
-#pragma unroll
-    for (int j = 0; j < NBPW; ++j) cb[j] = rb[j];
-    if (s + 1 < nstages) {
-      load_a(s + 1);
-      load_b(s + 1);
-    }
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const uint8_t *pa = smem + buf * TM * kRowB + (m * 16 + r16) * kRowB + q * 32;
-      Frag32 fa;
-      fa.lo = ld16(pa);
-      fa.hi = ld16(pa + 16);
-#pragma unroll
-      for (int j = 0; j < NBPW; ++j) acc[m][j] = mma32<Elem::BF16>(fa, cb[j], acc[m][j]);
-    }
-    if (s + 1 < nstages) store_a(buf ^ 1);
-    __syncthreads();
-  }
-
-  // logits -> LDS [TM][E]
-  float *sl = reinterpret_cast<float *>(smem);
-#pragma unroll
-  for (int j = 0; j < NBPW; ++j) {
-    const int e = (wave + 4 * j) * 16 + r16;
-    if (e < E) {
-      const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sl[(m * 16 + q * 4 + i) * E + e] = acc[m][j][i] + b;
-    }
-  }
-  __syncthreads();
-  topk_from_lds<TM, NC>(sl, selv, t0, T, E, k, ids, wout);
-}
-
-// bf16 router, split-K: the 4 waves of a workgroup take disjoint quarters of
-// h and each computes all TM x E partial logits straight from global memory
-// (no LDS, no barrier in the K loop; operands prefetched NBUF chunks ahead),
-// then the four partial sums are added in wave order through LDS, so the
-// result does not depend on timing.  NB = 16-expert column blocks (E <= 16 NB).
-template <int TM, int NB, int NBUF>
-__global__ __launch_bounds__(256) void router_bf16_splitk_kernel(
-    const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wr,
-    const float *__restrict__ bias, int T, int h, int E, int k,
-    int32_t *__restrict__ ids, float *__restrict__ wout) {
-  constexpr int MB = TM / 16;
-  constexpr int NC = (NB * 16 + 63) / 64;
-  __shared__ float red[4 * TM * NB * 16];
-  __shared__ float selv[4 * kMaxExperts];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane >> 4, r16 = lane & 15;
-  const int t0 = blockIdx.x * TM;
-  const int kq = h / 4;            // this wave's K range: [wave * kq, wave * kq + kq)
-  const int nchunks = kq / 32;     // 32 K elements per MFMA
+  const int e0 = blockIdx.x * EN, t0 = blockIdx.y * TM;
+  const int kq = h / 4;         // this wave's K range [wave * kq, wave * kq + kq)
+  const int nchunks = kq / 32;  // 32 K elements per MFMA
   const int kbase = wave * kq + q * 8;
 
   const uint16_t *arow[MB];
@@ -228,7 +122,7 @@ __global__ __launch_bounds__(256) void router_bf16_splitk_kernel(
   bool bvalid[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
-    const int e = n * 16 + r16;
+    const int e = e0 + n * 16 + r16;
     bvalid[n] = e < E;
     brow[n] = Wr + static_cast<int64_t>(bvalid[n] ? e : 0) * h + kbase;
   }
@@ -247,7 +141,6 @@ __global__ __launch_bounds__(256) void router_bf16_splitk_kernel(
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
-
 #pragma unroll
   for (int b = 0; b < NBUF; ++b)
     if (b < nchunks) load(b, b);
@@ -267,41 +160,46 @@ __global__ __launch_bounds__(256) void router_bf16_splitk_kernel(
     }
   }
 
-  // partial logits -> LDS, then a fixed-order sum over the 4 waves
-  constexpr int EP = NB * 16;
+  // partial logits -> LDS, fixed-order sum over the 4 waves -> global
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int n = 0; n < NB; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        red[(wave * TM + m * 16 + q * 4 + i) * EP + n * 16 + r16] = acc[m][n][i];
+        red[(wave * TM + m * 16 + q * 4 + i) * EN + n * 16 + r16] = acc[m][n][i];
   __syncthreads();
-  // sums into registers first, then (after a barrier) compacted to pitch E
-  constexpr int PER = (TM * EP + 255) / 256;
-  float sum[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = tid + 256 * j;
-    sum[j] = 0.0f;
-    if (i < TM * E) {
-      const int tt = i / E, e = i % E;
-      float v = red[tt * EP + e];
-      v += red[(TM + tt) * EP + e];
-      v += red[(2 * TM + tt) * EP + e];
-      v += red[(3 * TM + tt) * EP + e];
+  for (int i = tid; i < TM * EN; i += 256) {
+    const int tt = i / EN, el = i % EN;
+    const int t = t0 + tt, e = e0 + el;
+    if (t < T && e < E) {
+      float v = red[tt * EN + el];
+      v += red[(TM + tt) * EN + el];
+      v += red[(2 * TM + tt) * EN + el];
+      v += red[(3 * TM + tt) * EN + el];
       if (bias) v += bias[e];
-      sum[j] = v;
+      logits[static_cast<int64_t>(t) * E + e] = v;
     }
   }
+  __threadfence();  // this slice's logits are visible device-wide before the count
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = tid + 256 * j;
-    if (i < TM * E) red[i] = sum[j];
+  if (tid == 0) {
+    const int done = atomicAdd(&counters[blockIdx.y], 1);
+    is_last = done == static_cast<int>(gridDim.x) - 1;
   }
   __syncthreads();
-  topk_from_lds<TM, NC>(red, selv, t0, T, E, k, ids, wout);
+  if (!is_last) return;
+  __threadfence();
+  if (tid == 0) counters[blockIdx.y] = 0;
+  for (int i = tid; i < TM * E; i += 256) {
+    const int tt = i / E, e = i % E;
+    const int t = t0 + tt;
+    red[i] = t < T ? __hip_atomic_load(&logits[static_cast<int64_t>(t) * E + e], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0.0f;
+  }
+  __syncthreads();
+  topk_from_lds<TM, kMaxExperts / 64>(red, selv, t0, T, E, k, ids, wout);
 }
 
 // fp32 router for small layers: one (token, expert) dot product per thread.
@@ -330,9 +228,12 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 
 }  // namespace
 
+int router_blocks(int T) { return (T + 15) / 16; }
+
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
-                         int32_t *ids, float *w, hipStream_t s) {
+                         float *logits, int32_t *counters, int32_t *ids, float *w,
+                         hipStream_t s) {
   if (f32) {
     constexpr int TM = 16;
     router_f32_kernel<TM><<<(T + TM - 1) / TM, 256, 0, s>>>(
@@ -342,18 +243,20 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   }
   const uint16_t *X = static_cast<const uint16_t *>(x);
   const uint16_t *W = static_cast<const uint16_t *>(wr);
-  if (E <= 64) {
-    if (T <= 4096)
-      router_bf16_splitk_kernel<16, 4, 4><<<(T + 15) / 16, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
-    else
-      router_bf16_splitk_kernel<32, 4, 2><<<(T + 31) / 32, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
-  } else if (E <= 256) {
-    if (T <= 4096)
-      router_bf16_splitk_kernel<16, 16, 2><<<(T + 15) / 16, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
-    else
-      router_bf16_splitk_kernel<32, 16, 1><<<(T + 31) / 32, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
+  // token blocks of 16 (64 for long batches), expert slices sized so that a
+  // batch launches a few hundred workgroups
+  if (T > 4096) {
+    const dim3 grid((E + 63) / 64, (T + 63) / 64);
+    router_bf16_kernel<64, 64, 2><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
+  } else if (E <= 64 || T <= 256) {
+    const dim3 grid((E + 15) / 16, (T + 15) / 16);
+    router_bf16_kernel<16, 16, 4><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
+  } else if (T <= 1024) {
+    const dim3 grid((E + 31) / 32, (T + 15) / 16);
+    router_bf16_kernel<16, 32, 4><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
   } else {
-    router_bf16_kernel<32, 8><<<(T + 31) / 32, 256, 0, s>>>(X, W, bias, T, h, E, k, ids, w);
+    const dim3 grid((E + 63) / 64, (T + 15) / 16);
+    router_bf16_kernel<16, 64, 2><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
   }
   return hipGetLastError();
 }
