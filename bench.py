@@ -33,11 +33,28 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of all kernel sources: a stored counter reading is only reported
+    while the code it was taken on is unchanged."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "kernels.h"):
-        with open(os.path.join(ROOT, "expert_side_attention_amd", "csrc", f), "rb") as fh:
+    d = os.path.join(ROOT, "expert_side_attention_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of a known size (for scaling the HBM
+    byte counters of a profiler run)."""
+    import torch
+    n = mib * 1024 * 1024
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
 def work_model(s, counts):
@@ -142,7 +159,12 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (profiler calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the layer runs on a single MI355X "
               f"(--gpus {args.gpus} is not supported).", file=sys.stderr)
@@ -238,6 +260,7 @@ def main():
             t = json.load(f)
         if t.get("kernel_source_hash") == kernel_source_hash():
             traffic = t.get("hbm_bytes_per_launch")
+    res_hash = kernel_source_hash()
     value = shape.T / (ms_step * 1e-3)
     fwd_gbs = model["forward_bytes"] / (ms_step * 1e-3) / 1e9
     res = {
@@ -278,6 +301,7 @@ def main():
                     "micro_batches": nmb, "ms_serial_one_stream": round(ms_serial, 5),
                     "stage_ms": stages},
         "cpu_baseline": None,
+        "kernel_source_hash": res_hash,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")

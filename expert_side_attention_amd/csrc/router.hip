@@ -38,13 +38,13 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
 
 // Top-k over the logits of TM tokens held in LDS (row pitch E), one wave per
 // token at a time.  NC = candidates per lane (E <= 64 * NC).
-template <int TM, int NC>
+template <int TM, int NC, int WAVES = 4>
 __device__ void topk_from_lds(const float *sl, float *selv, int t0, int T,
                               int E, int k, int32_t *ids, float *wout) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   float *mysel = selv + wave * kMaxExperts;
-  for (int tt = wave; tt < TM; tt += 4) {
+  for (int tt = wave; tt < TM; tt += WAVES) {
     const int t = t0 + tt;
     if (t >= T) break;
     const float *row = sl + tt * E;
@@ -82,31 +82,32 @@ __device__ void topk_from_lds(const float *sl, float *selv, int t0, int T,
 }
 
 // bf16 router.  The grid is (expert slices of EN) x (token blocks of TM), so
-// even small batches spread over many CUs.  Inside a workgroup the 4 waves
-// take disjoint quarters of h and compute all TM x EN partial logits with
+// even small batches spread over many CUs.  Inside a workgroup the WAVES
+// waves take disjoint slices of h and compute all TM x EN partial logits with
 // operands loaded straight from global memory into MFMA registers (no LDS,
 // no barrier in the K loop, NBUF chunks of prefetch); the partial sums are
 // added in wave order, so the logits do not depend on timing.  Each
 // workgroup stores its logit slice; the last one to finish a token block
 // (device-scope counter) runs the top-k for that block and resets the
-// counter to 0 for the next call.
-template <int TM, int EN, int NBUF>
-__global__ __launch_bounds__(256) void router_bf16_kernel(
+// counter to 0 for the next call.  EMAX bounds E (top-k LDS size).
+template <int TM, int EN, int NBUF, int WAVES, int EMAX>
+__global__ __launch_bounds__(WAVES * 64) void router_bf16_kernel(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wr,
     const float *__restrict__ bias, int T, int h, int E, int k,
     float *__restrict__ logits, int32_t *__restrict__ counters,
     int32_t *__restrict__ ids, float *__restrict__ wout) {
   constexpr int MB = TM / 16, NB = EN / 16;
-  constexpr int RED = 4 * TM * EN;
-  constexpr int TOPK = TM * kMaxExperts;
+  constexpr int THREADS = WAVES * 64;
+  constexpr int RED = WAVES * TM * EN;
+  constexpr int TOPK = TM * EMAX;
   __shared__ float red[RED > TOPK ? RED : TOPK];
-  __shared__ float selv[4 * kMaxExperts];
+  __shared__ float selv[WAVES * kMaxExperts];
   __shared__ int is_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const int e0 = blockIdx.x * EN, t0 = blockIdx.y * TM;
-  const int kq = h / 4;         // this wave's K range [wave * kq, wave * kq + kq)
+  const int kq = h / WAVES;     // this wave's K range [wave * kq, wave * kq + kq)
   const int nchunks = kq / 32;  // 32 K elements per MFMA
   const int kbase = wave * kq + q * 8;
 
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
     }
   }
 
-  // partial logits -> LDS, fixed-order sum over the 4 waves -> global
+  // partial logits -> LDS, fixed-order sum over the waves -> global
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -169,14 +170,13 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
       for (int i = 0; i < 4; ++i)
         red[(wave * TM + m * 16 + q * 4 + i) * EN + n * 16 + r16] = acc[m][n][i];
   __syncthreads();
-  for (int i = tid; i < TM * EN; i += 256) {
+  for (int i = tid; i < TM * EN; i += THREADS) {
     const int tt = i / EN, el = i % EN;
     const int t = t0 + tt, e = e0 + el;
     if (t < T && e < E) {
       float v = red[tt * EN + el];
-      v += red[(TM + tt) * EN + el];
-      v += red[(2 * TM + tt) * EN + el];
-      v += red[(3 * TM + tt) * EN + el];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) v += red[(w * TM + tt) * EN + el];
       if (bias) v += bias[e];
       logits[static_cast<int64_t>(t) * E + e] = v;
     }
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
   if (!is_last) return;
   __threadfence();
   if (tid == 0) counters[blockIdx.y] = 0;
-  for (int i = tid; i < TM * E; i += 256) {
+  for (int i = tid; i < TM * E; i += THREADS) {
     const int tt = i / E, e = i % E;
     const int t = t0 + tt;
     red[i] = t < T ? __hip_atomic_load(&logits[static_cast<int64_t>(t) * E + e], __ATOMIC_RELAXED,
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(
                    : 0.0f;
   }
   __syncthreads();
-  topk_from_lds<TM, kMaxExperts / 64>(red, selv, t0, T, E, k, ids, wout);
+  topk_from_lds<TM, EMAX / 64, WAVES>(red, selv, t0, T, E, k, ids, wout);
 }
 
 // fp32 router for small layers: one (token, expert) dot product per thread.
@@ -244,20 +244,31 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   const uint16_t *X = static_cast<const uint16_t *>(x);
   const uint16_t *W = static_cast<const uint16_t *>(wr);
   // token blocks of 16 (64 for long batches), expert slices sized so that a
-  // batch launches a few hundred workgroups
-  if (T > 4096) {
-    const dim3 grid((E + 63) / 64, (T + 63) / 64);
-    router_bf16_kernel<64, 64, 2><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
+  // batch launches a few hundred workgroups, K split over 8 waves (4 for the
+  // 64-token blocks, whose partial sums would not fit LDS otherwise)
+#define AFD_ROUTER(TM, EN, NBUF, WAVES, EMAX)                                          \
+  router_bf16_kernel<TM, EN, NBUF, WAVES, EMAX>                                       \
+      <<<dim3((E + EN - 1) / EN, (T + TM - 1) / TM), WAVES * 64, 0, s>>>(             \
+          X, W, bias, T, h, E, k, logits, counters, ids, w)
+  // each wave's K slice must be whole 32-element chunks: 8 waves need
+  // h % 256 == 0, 4 waves h % 128 == 0 (always true here)
+  const bool k8 = h % 256 == 0;
+  if (E > 256) {
+    if (k8) AFD_ROUTER(16, 64, 4, 8, 512);
+    else AFD_ROUTER(16, 64, 4, 4, 512);
+  } else if (T > 4096) {
+    AFD_ROUTER(64, 64, 4, 4, 256);
   } else if (E <= 64 || T <= 256) {
-    const dim3 grid((E + 15) / 16, (T + 15) / 16);
-    router_bf16_kernel<16, 16, 4><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
+    if (k8) AFD_ROUTER(16, 16, 8, 8, 256);
+    else AFD_ROUTER(16, 16, 8, 4, 256);
   } else if (T <= 1024) {
-    const dim3 grid((E + 31) / 32, (T + 15) / 16);
-    router_bf16_kernel<16, 32, 4><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
+    if (k8) AFD_ROUTER(16, 32, 6, 8, 256);
+    else AFD_ROUTER(16, 32, 6, 4, 256);
   } else {
-    const dim3 grid((E + 63) / 64, (T + 15) / 16);
-    router_bf16_kernel<16, 64, 2><<<grid, 256, 0, s>>>(X, W, bias, T, h, E, k, logits, counters, ids, w);
+    if (k8) AFD_ROUTER(16, 64, 4, 8, 256);
+    else AFD_ROUTER(16, 64, 4, 4, 256);
   }
+#undef AFD_ROUTER
   return hipGetLastError();
 }
 
