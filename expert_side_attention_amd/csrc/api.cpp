@@ -52,13 +52,13 @@ struct afd_ffn_handle {
   int device;
   int elem;    // 0 f32, 1 bf16, 2 fp8 (GEMM operand type)
   int zpitch;  // Z row length in elements: max(I, I_s)
-  int tiles_cap;
+  int tiles_cap, big_cap;
   void *ws;
   size_t ws_bytes;
-  int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *counters;
+  int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *num_big, *counters;
   int32_t *router_counters;
   float *topk_w, *logits;
-  afd::Tile *tiles;
+  afd::Tile *tiles, *tiles_big;
   uint8_t *xq;
   float *xs;
   uint8_t *z;
@@ -73,10 +73,16 @@ struct afd_ffn_handle {
 
 namespace {
 
+// Upper bound of the small-tile list: every group adds at most one partial
+// tile to R / bm full ones.
 int64_t tiles_upper_bound(int64_t T, int k, int E, int S, int bm) {
-  const int64_t tk = T * k;
-  const int64_t routed = (tk + bm - 1) / bm + (tk < E ? tk : E);
-  return routed + S * ((T + bm - 1) / bm);
+  const int64_t rows = T * k + S * T;
+  const int64_t groups = (T * k < E ? T * k : E) + S;
+  return rows / bm + groups;
+}
+// Upper bound of the big-tile list: every big tile holds more than bm / 2 rows.
+int64_t big_tiles_upper_bound(int64_t T, int k, int S, int bm) {
+  return (T * k + S * T) * 2 / bm + 1;
 }
 
 int validate_config(const afd_ffn_config *c) {
@@ -173,6 +179,7 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
   const int64_t T = cfg->max_tokens, k = cfg->top_k, E = cfg->num_experts;
   const int64_t hd = cfg->hidden;
   h->tiles_cap = static_cast<int>(tiles_upper_bound(T, cfg->top_k, cfg->num_experts, S, 16));
+  h->big_cap = static_cast<int>(big_tiles_upper_bound(T, cfg->top_k, S, 256));
 
   const int64_t R = T * k + S * T;  // dispatched + shared rows
   const int zes = h->elem == 0 ? 4 : (h->elem == 1 ? 2 : 1);
@@ -189,10 +196,12 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
       {reinterpret_cast<void **>(&h->counts), sizeof(int32_t) * E},
       {reinterpret_cast<void **>(&h->offsets), sizeof(int32_t) * (E + 1)},
       {reinterpret_cast<void **>(&h->num_tiles), sizeof(int32_t)},
+      {reinterpret_cast<void **>(&h->num_big), sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->counters), 2 * sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->router_counters), sizeof(int32_t) * afd::router_blocks(T)},
       {reinterpret_cast<void **>(&h->logits), sizeof(float) * T * E},
       {reinterpret_cast<void **>(&h->tiles), sizeof(afd::Tile) * h->tiles_cap},
+      {reinterpret_cast<void **>(&h->tiles_big), sizeof(afd::Tile) * h->big_cap},
       {reinterpret_cast<void **>(&h->z), static_cast<size_t>(R) * h->zpitch * zes},
       {reinterpret_cast<void **>(&h->y), static_cast<size_t>(R) * hd * yes},
   };
@@ -245,16 +254,29 @@ void afd_ffn_destroy(afd_ffn_handle *h) {
   delete h;
 }
 
-static hipError_t launch_gemms(afd::GemmKind kind, const afd::GemmPlan &plan, int elem,
-                               const afd::GemmArgs &a, hipStream_t s) {
-  switch (plan.kernel) {
+// One GEMM stage: the small-tile list on its kernel, then (if the plan has
+// one) the big-tile list on the compute-bound kernel.
+static hipError_t launch_gemms(afd_ffn_handle *h, afd::GemmKind kind, const afd::GemmPlan &plan,
+                               afd::GemmArgs a, int64_t T, hipStream_t s) {
+  const afd_ffn_config &c = h->cfg;
+  a.tiles = h->tiles;
+  a.num_tiles = h->num_tiles;
+  a.tiles_ub = static_cast<int>(
+      tiles_upper_bound(T, c.top_k, c.num_experts, c.num_shared, plan.tiles.bm_small));
+  hipError_t e;
+  switch (plan.small_kernel) {
     case afd::GemmKernel::Stream:
-      return afd::launch_gemm_stream(kind, elem, plan.bm, a, s);
-    case afd::GemmKernel::Prefill:
-      return afd::launch_gemm_prefill(kind, a, s);
+      e = afd::launch_gemm_stream(kind, h->elem, plan.tiles.bm_small, a, s);
+      break;
     default:
-      return afd::launch_gemm(kind, elem, plan.bm, a, s);
+      e = afd::launch_gemm(kind, h->elem, plan.tiles.bm_small, a, s);
+      break;
   }
+  if (e != hipSuccess || plan.tiles.bm_big == 0) return e;
+  a.tiles = h->tiles_big;
+  a.num_tiles = h->num_big;
+  a.tiles_ub = static_cast<int>(big_tiles_upper_bound(T, c.top_k, c.num_shared, plan.tiles.bm_big));
+  return afd::launch_gemm_prefill(kind, a, s);
 }
 
 static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
@@ -294,8 +316,9 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
 
   const afd::GemmPlan plan = afd::gemm_plan(h->elem, Ti, k, E);
   ev = prof_begin(h, AFD_STAGE_DISPATCH, s);
-  e = afd::launch_dispatch(h->ids, Ti, k, E, S, plan.bm, h->counts, h->offsets, h->perm,
-                           h->slot_row, h->tiles, h->num_tiles, h->counters, 2, s);
+  e = afd::launch_dispatch(h->ids, Ti, k, E, S, plan.tiles, h->counts, h->offsets, h->perm,
+                           h->slot_row, h->tiles, h->num_tiles, h->tiles_big, h->num_big,
+                           h->counters, 2, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
 
@@ -333,16 +356,13 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   g.Ns = S > 0 ? c.shared_inter : c.inter;
   g.Ks = hd;
   g.E = E;
-  g.tiles = h->tiles;
-  g.num_tiles = h->num_tiles;
-  g.tiles_ub = static_cast<int>(tiles_upper_bound(T, k, E, S, plan.bm));
   g.work_counter = h->counters;
   g.C = h->z;
   g.c_pitch = static_cast<int64_t>(h->zpitch) * zes;
   g.c_scale = h->zs;
   g.c_scale_pitch = h->zpitch / 128;
   ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
-  e = launch_gemms(afd::GemmKind::GateUp, plan, h->elem, g, s);
+  e = launch_gemms(h, afd::GemmKind::GateUp, plan, g, T, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
 
@@ -369,7 +389,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   d.c_scale = nullptr;
   d.work_counter = h->counters + 1;
   ev = prof_begin(h, AFD_STAGE_DOWN, s);
-  e = launch_gemms(afd::GemmKind::Down, plan, h->elem, d, s);
+  e = launch_gemms(h, afd::GemmKind::Down, plan, d, T, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
 

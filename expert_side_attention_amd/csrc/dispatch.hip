@@ -51,10 +51,11 @@ __device__ int block_exclusive_scan(int v, int *wsum, int *total) {
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_kernel(
-    const int32_t *__restrict__ ids, int T, int k, int E, int S, int bm,
+    const int32_t *__restrict__ ids, int T, int k, int E, int S, TilePlan tp,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ perm, int32_t *__restrict__ slot_row,
-    Tile *__restrict__ tiles, int32_t *__restrict__ num_tiles,
+    Tile *__restrict__ tiles_s, int32_t *__restrict__ num_s,
+    Tile *__restrict__ tiles_b, int32_t *__restrict__ num_b,
     int32_t *__restrict__ counters, int ncounters) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int run[kMaxExperts];
@@ -81,28 +82,54 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
     run[tid] = off;
   }
   if (tid == 0) offsets[E] = total;
-  const int nt = tid < E ? (c + bm - 1) / bm : 0;
-  int routed_tiles = 0;
-  const int tbase = block_exclusive_scan(nt, wsum, &routed_tiles);
-  for (int m = 0; m < nt; ++m) {
+  // Tile lists.  Group g < E is routed expert g (its rows start at offsets[g]),
+  // group E + s is shared expert s (T rows from T*k + s*T).  With a big-tile
+  // list, a group of at least big_min rows gets full big tiles, plus one
+  // partial big tile if the remainder exceeds half a big tile; all other
+  // rows go to small tiles.
+  const int G = E + S;
+  int gc = 0, g0 = 0;
+  if (tid < E) {
+    gc = c;
+    g0 = off;
+  } else if (tid < G) {
+    gc = T;
+    g0 = static_cast<int>(Tk) + (tid - E) * T;
+  }
+  int nbig = 0, rem = gc;
+  if (tid < G && tp.bm_big > 0 && gc >= tp.big_min) {
+    nbig = gc / tp.bm_big;
+    rem = gc - nbig * tp.bm_big;
+    if (rem * 2 > tp.bm_big) {
+      ++nbig;
+      rem = 0;
+    }
+  }
+  const int nsmall = tid < G ? (rem + tp.bm_small - 1) / tp.bm_small : 0;
+  int tot_b = 0, tot_s = 0;
+  const int bbase = block_exclusive_scan(nbig, wsum, &tot_b);
+  const int sbase = block_exclusive_scan(nsmall, wsum, &tot_s);
+  for (int m = 0; m < nbig; ++m) {
     Tile t;
     t.group = tid;
-    t.row0 = off + m * bm;
-    t.rows = min(bm, c - m * bm);
+    t.row0 = g0 + m * tp.bm_big;
+    t.rows = min(tp.bm_big, gc - m * tp.bm_big);
     t.pad = 0;
-    tiles[tbase + m] = t;
+    tiles_b[bbase + m] = t;
   }
-  const int ns = (T + bm - 1) / bm;
-  for (int i = tid; i < S * ns; i += kThreads) {
-    const int sg = i / ns, m = i % ns;
+  const int sfirst = g0 + (gc - rem);
+  for (int m = 0; m < nsmall; ++m) {
     Tile t;
-    t.group = E + sg;
-    t.row0 = static_cast<int>(Tk) + sg * T + m * bm;
-    t.rows = min(bm, T - m * bm);
+    t.group = tid;
+    t.row0 = sfirst + m * tp.bm_small;
+    t.rows = min(tp.bm_small, rem - m * tp.bm_small);
     t.pad = 0;
-    tiles[routed_tiles + i] = t;
+    tiles_s[sbase + m] = t;
   }
-  if (tid == 0) *num_tiles = routed_tiles + S * ns;
+  if (tid == 0) {
+    *num_s = tot_s;
+    if (num_b) *num_b = tot_b;
+  }
   if (tid < ncounters) counters[tid] = 0;
   __syncthreads();
 
@@ -140,13 +167,13 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
 }  // namespace
 
 hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
-                           int bm, int32_t *counts, int32_t *offsets,
-                           int32_t *perm, int32_t *slot_row, Tile *tiles,
-                           int32_t *num_tiles, int32_t *counters,
-                           int ncounters, hipStream_t s) {
-  dispatch_kernel<<<1, kThreads, 0, s>>>(ids, T, k, E, S, bm, counts, offsets,
-                                         perm, slot_row, tiles, num_tiles,
-                                         counters, ncounters);
+                           const TilePlan &tp, int32_t *counts, int32_t *offsets,
+                           int32_t *perm, int32_t *slot_row, Tile *tiles_s,
+                           int32_t *num_s, Tile *tiles_b, int32_t *num_b,
+                           int32_t *counters, int ncounters, hipStream_t s) {
+  dispatch_kernel<<<1, kThreads, 0, s>>>(ids, T, k, E, S, tp, counts, offsets,
+                                         perm, slot_row, tiles_s, num_s, tiles_b,
+                                         num_b, counters, ncounters);
   return hipGetLastError();
 }
 

@@ -296,15 +296,19 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 GemmPlan gemm_plan(int elem, int T, int k, int E) {
-  if (elem == 0) return {32, GemmKernel::Tiled};
+  if (elem == 0) return {{32, 0, 0}, GemmKernel::Tiled};
   // rows per expert on average decide the regime: a few dozen rows per
   // expert -> stream the weights once with a tile that holds all of them;
-  // hundreds of rows -> compute-bound 256-row tiles (bf16)
+  // hundreds of rows (bf16) -> experts' 256-row blocks go to the
+  // compute-bound kernel and small experts / small remainders (<= 128 rows)
+  // to the streaming kernel
   const int64_t avg = (static_cast<int64_t>(T) * k + E - 1) / E;
-  if (avg <= 48) return {64, GemmKernel::Stream};
-  if (avg <= 112) return {128, GemmKernel::Stream};
-  if (elem == 1) return {256, GemmKernel::Prefill};
-  return {64, GemmKernel::Tiled};
+  if (avg <= 48) return {{64, 0, 0}, GemmKernel::Stream};
+  if (avg <= 112 || elem == 2) {
+    if (elem == 2 && avg > 112) return {{64, 0, 0}, GemmKernel::Tiled};
+    return {{128, 0, 0}, GemmKernel::Stream};
+  }
+  return {{128, 256, 129}, GemmKernel::Stream};
 }
 
 hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,

@@ -11,8 +11,10 @@
 // lane).  Per stage each wave reads 32 KB of operands from LDS for 64 MFMAs,
 // half the LDS bandwidth at full MFMA rate.
 //
-// Operands go global -> registers -> LDS, double-buffered; the next stage's
-// global loads are in flight during the current stage's MFMAs.  LDS rows are
+// Operands go global -> registers -> LDS, double-buffered: during stage s
+// the MFMAs read buffer s % 2 while stage s+1 (already in registers) is
+// written to the other buffer and stage s+2 is loaded, in four parts
+// interleaved with the four MFMA k-steps.  The main loop has no branches.  LDS rows are
 // 128 bytes with the 16-byte chunk index XOR-ed by (row / 2) mod 8, so the
 // 32 rows an MFMA operand read touches spread over all banks.
 //
@@ -83,16 +85,19 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
   const uint8_t *B0 = (shared ? p.sb0 : p.b0) + gi * mat;
   const uint8_t *B1 = SWIGLU ? (shared ? p.sb1 : p.b1) + gi * mat : nullptr;
 
-  // per-thread load slots: chunk c = tid + 256 i, row c / 8, 16-byte chunk c % 8
+  // Per-thread load slots: chunk c = tid + 256 i, row c / 8, 16-byte chunk
+  // c % 8.  Rows past the tile's end read a valid row instead (the rows of an
+  // MFMA tile are independent and those results are never stored), and
+  // weight rows past N (partial last column tile) read row N - 1, so the main
+  // loop has no branches.
+  const int src_first = rowsrc[0];
   const uint8_t *asrc[8];
   const uint8_t *bsrc[8];
-  bool aval[8], bval[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-    const int src = rowsrc[row];
-    aval[i] = src >= 0;
-    asrc[i] = p.A + static_cast<int64_t>(aval[i] ? src : 0) * p.a_pitch + ch * 16;
+    const int src = rowsrc[row] >= 0 ? rowsrc[row] : src_first;
+    asrc[i] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
     const uint8_t *base;
     int n;
     if (SWIGLU) {
@@ -102,20 +107,21 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
       base = B0;
       n = n0 + row;
     }
-    bval[i] = n < N;  // a partial last column tile (down, N % 256 != 0)
-    bsrc[i] = base + static_cast<int64_t>(bval[i] ? n : 0) * krow + ch * 16;
+    bsrc[i] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16;
   }
   u32x4 ra[8], rb[8];
-  auto gload = [&](int s) {
+  // slots are moved in 4 parts of 2 (A) + 2 (B) so that LDS stores and
+  // global loads interleave with the 4 MFMA k-steps of a stage
+  auto gload_part = [&](int part, int s) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = aval[i] ? ld16(asrc[i] + static_cast<int64_t>(s) * kRow) : u32x4{0, 0, 0, 0};
-      rb[i] = bval[i] ? ld16(bsrc[i] + static_cast<int64_t>(s) * kRow) : u32x4{0, 0, 0, 0};
+    for (int i = 2 * part; i < 2 * part + 2; ++i) {
+      ra[i] = ld16(asrc[i] + static_cast<int64_t>(s) * kRow);
+      rb[i] = ld16(bsrc[i] + static_cast<int64_t>(s) * kRow);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore_part = [&](int part, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 2 * part; i < 2 * part + 2; ++i) {
       const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
       st16(ldsA + buf * kBM * kRow + swz(row, ch), ra[i]);
       st16(ldsB + buf * kBW * kRow + swz(row, ch), rb[i]);
@@ -128,8 +134,6 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
 
-  // row blocks of this wave that hold valid rows
-  const int mb_active = min(4, max(0, (rows - wr * 128 + 31) >> 5));
   // weight rows of n-block n for this wave
   int wrow[4];
 #pragma unroll
@@ -137,33 +141,40 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
     wrow[n] = SWIGLU ? ((n >> 1) * (kBW / 2) + wc * 64 + (n & 1) * 32 + r32)
                      : (wc * 128 + n * 32 + r32);
 
-  gload(0);
-  lstore(0);
-  if (nst > 1) gload(1);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) gload_part(part, 0);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) lstore_part(part, 0);
+  if (nst > 1) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) gload_part(part, 1);
+  }
   __syncthreads();
   for (int s = 0; s < nst; ++s) {
     const int buf = s & 1;
     const uint8_t *la = ldsA + buf * kBM * kRow;
     const uint8_t *lb = ldsB + buf * kBW * kRow;
+    const bool more = s + 1 < nst, more2 = s + 2 < nst;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int ch = 2 * ks + g;
-      bf16x8 bfr[4];
+      bf16x8 bfr[4], afr[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) bfr[n] = bitcast<bf16x8>(ld16(lb + swz(wrow[n], ch)));
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (m < mb_active) {
-          const bf16x8 afr = bitcast<bf16x8>(ld16(la + swz(wr * 128 + m * 32 + r32, ch)));
+      for (int m = 0; m < 4; ++m)
+        afr[m] = bitcast<bf16x8>(ld16(la + swz(wr * 128 + m * 32 + r32, ch)));
 #pragma unroll
-          for (int n = 0; n < 4; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[n], acc[m][n], 0, 0, 0);
-        }
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[m], bfr[n], acc[m][n], 0, 0, 0);
+      // stage s+1 (loaded during the previous stage) into the other buffer,
+      // then reuse the registers for stage s+2
+      if (more) {
+        lstore_part(ks, buf ^ 1);
+        if (more2) gload_part(ks, s + 2);
       }
-    }
-    if (s + 1 < nst) {
-      lstore(buf ^ 1);  // stage s+1 (loaded during the previous stage)
-      if (s + 2 < nst) gload(s + 2);
     }
     __syncthreads();
   }

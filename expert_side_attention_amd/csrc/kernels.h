@@ -29,14 +29,22 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
                          float *logits, int32_t *counters, int32_t *ids, float *w,
                          hipStream_t s);
 
-// Histogram, scan and stable scatter of the (token, slot) pairs; GEMM tile
-// list for row tiles of `bm` rows (routed experts, then S shared groups).
-// Also zeroes `counters[0..ncounters)` (the GEMMs' work counters).
+// Row-tile lists of a forward: small tiles (bm_small rows) and, if
+// bm_big > 0, big tiles (bm_big rows) for groups of at least big_min rows.
+struct TilePlan {
+  int bm_small;
+  int bm_big;
+  int big_min;
+};
+
+// Histogram, scan and stable scatter of the (token, slot) pairs, and the
+// two GEMM tile lists (routed experts, then the S shared groups).  Also
+// zeroes `counters[0..ncounters)` (the GEMMs' work counters).
 hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
-                           int bm, int32_t *counts, int32_t *offsets,
-                           int32_t *perm, int32_t *slot_row, Tile *tiles,
-                           int32_t *num_tiles, int32_t *counters,
-                           int ncounters, hipStream_t s);
+                           const TilePlan &tp, int32_t *counts, int32_t *offsets,
+                           int32_t *perm, int32_t *slot_row, Tile *tiles_s,
+                           int32_t *num_s, Tile *tiles_b, int32_t *num_b,
+                           int32_t *counters, int ncounters, hipStream_t s);
 
 hipError_t launch_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
                               uint8_t *q, float *sc, hipStream_t s);
@@ -74,12 +82,12 @@ struct GemmArgs {
   int c_scale_pitch;
 };
 
-// GEMM variant for a forward: row tile height (the dispatch kernel builds
-// the tile list with it) and which kernel family runs the two GEMMs.
+// GEMM plan of a forward: the tile lists and the kernel family that runs
+// each (big tiles always go to the compute-bound prefill kernel).
 enum class GemmKernel { Tiled = 0, Stream = 1, Prefill = 2 };
 struct GemmPlan {
-  int bm;
-  GemmKernel kernel;
+  TilePlan tiles;
+  GemmKernel small_kernel;
 };
 GemmPlan gemm_plan(int elem, int T, int k, int E);
 
