@@ -111,6 +111,10 @@ int validate_config(const afd_ffn_config *c) {
     return fail(AFD_ERR_INVALID_ARG, "max_tokens %d outside [1, 2^20]", c->max_tokens);
   if (static_cast<int64_t>(c->max_tokens) * (c->top_k + c->num_shared) >= (1LL << 31))
     return fail(AFD_ERR_INVALID_ARG, "max_tokens * (top_k + num_shared) must be < 2^31");
+  // one expert matrix is addressed with 32-bit byte offsets inside kernels
+  if (static_cast<int64_t>(c->hidden) * c->inter * 4 >= (1LL << 32) ||
+      static_cast<int64_t>(c->hidden) * c->shared_inter * 4 >= (1LL << 32))
+    return fail(AFD_ERR_UNSUPPORTED, "an expert matrix must be smaller than 4 GiB in fp32");
   if (c->has_router_bias != 0 && c->has_router_bias != 1)
     return fail(AFD_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
   return AFD_OK;

@@ -6,17 +6,18 @@
 //
 // Tile: 256 rows x 256 weight rows per workgroup (gate/up: 128 gate + 128 up
 // rows, i.e. 128 output columns of z; down: 256 output columns), K in
-// 64-element stages.  Four waves in a 2 x 2 grid each own 128 rows x 128
-// weight rows = 4 x 4 tiles of 32x32x16 MFMAs (256 fp32 accumulators per
-// lane).  Per stage each wave reads 32 KB of operands from LDS for 64 MFMAs,
-// half the LDS bandwidth at full MFMA rate.
+// 32-element (64-byte) stages.  Eight waves (two per SIMD) in a 2 x 4 grid
+// each own 128 rows x 64 weight rows = 4 x 2 tiles of 32x32x16 MFMAs (128
+// fp32 accumulators per lane); for gate/up a wave's two column blocks are a
+// gate block and the up block of the same columns.
 //
-// Operands go global -> registers -> LDS, double-buffered: during stage s
-// the MFMAs read buffer s % 2 while stage s+1 (already in registers) is
-// written to the other buffer and stage s+2 is loaded, in four parts
-// interleaved with the four MFMA k-steps.  The main loop has no branches.  LDS rows are
-// 128 bytes with the 16-byte chunk index XOR-ed by (row / 2) mod 8, so the
-// 32 rows an MFMA operand read touches spread over all banks.
+// Operands move with direct-to-LDS loads (global_load_lds, no staging
+// registers) into a ring of 4 stage slots, so three stages (96 KB) are in
+// flight per workgroup while the MFMAs read the fourth: with one stage in
+// flight the loads could not keep up with the MFMAs.  Ordering uses
+// explicit vmcnt waits plus a bare s_barrier per stage (a full workgroup
+// fence would drain every outstanding load).  LDS rows are 64 bytes with the
+// 16-byte chunk index XOR-ed by (row / 4) % 4 against bank conflicts.
 //
 // Tile order: row tiles are dealt round-robin to the 8 XCDs (workgroup ids
 // go to XCDs round-robin) and all column tiles of a row tile run on one XCD,
@@ -29,27 +30,38 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256;   // rows per tile
-constexpr int kBW = 256;   // weight rows per tile
-constexpr int kRow = 128;  // bytes per LDS row (one K stage)
+constexpr int kBM = 256;    // rows per tile
+constexpr int kBW = 256;    // weight rows per tile
+constexpr int kStage = 64;  // bytes per row per K stage (32 bf16)
+constexpr int kRing = 4;    // LDS ring of stages (3 in flight)
+constexpr int kSlot = (kBM + kBW) * kStage;  // 32 KB
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRow + ((chunk ^ ((row >> 1) & 7)) << 4);
+// byte offset of 16-byte chunk `chunk` (0..3) of LDS row `row`: the chunk
+// index is XOR-ed with (row / 4) % 4 so that the 16 rows one MFMA operand
+// read touches per half-wave hit 16 different 4-bank groups
+__device__ __forceinline__ int swz64(int row, int chunk) {
+  return row * kStage + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// One 16-byte-per-lane direct-to-LDS load: lane i of the wave writes LDS
+// bytes [16 i, 16 i + 16) above the wave-uniform `lds_dst`.
+__device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_dst) {
+  // C-style casts: generic -> global / LDS address-space pointers
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+}
+
 template <bool SWIGLU>
-__global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
-  extern __shared__ __align__(16) uint8_t lds[];  // 2 x (A 32 KB + B 32 KB)
+__global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
+  extern __shared__ __align__(16) uint8_t lds[];  // kRing x (A 16 KB + B 16 KB)
   __shared__ int rowsrc[kBM];
-  uint8_t *ldsA = lds;                       // [2][256][128]
-  uint8_t *ldsB = lds + 2 * kBM * kRow;      // [2][256][128]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave >> 2, wc = wave & 3;   // 2 x 4 waves: 128 rows x 64 weight rows each
   const int r32 = lane & 31, g = lane >> 5;
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;  // output columns per tile
 
@@ -80,104 +92,89 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
   __syncthreads();
 
   const int64_t krow = static_cast<int64_t>(K) * 2;
-  const int nst = static_cast<int>(krow / kRow);
+  const int nst = static_cast<int>(krow / kStage);
   const int64_t mat = static_cast<int64_t>(N) * krow;
   const uint8_t *B0 = (shared ? p.sb0 : p.b0) + gi * mat;
-  const uint8_t *B1 = SWIGLU ? (shared ? p.sb1 : p.b1) + gi * mat : nullptr;
+  const uint8_t *B1 = SWIGLU ? (shared ? p.sb1 : p.b1) + gi * mat : B0;
 
-  // Per-thread load slots: chunk c = tid + 256 i, row c / 8, 16-byte chunk
-  // c % 8.  Rows past the tile's end read a valid row instead (the rows of an
-  // MFMA tile are independent and those results are never stored), and
-  // weight rows past N (partial last column tile) read row N - 1, so the main
-  // loop has no branches.
+  // Each wave moves rows [32 wave, 32 wave + 32) of the A stage and of the
+  // B stage: two 1 KB direct-to-LDS loads each (16 rows of 64 bytes per
+  // load).  Lane i fills LDS row 16 h + i / 4, position i % 4, which holds
+  // the row's 16-byte chunk (i % 4) ^ ((row / 4) % 4) (bank swizzle).
+  // Rows past the tile's end load a valid row (rows of an MFMA tile are
+  // independent; those results are never stored); weight rows past N (a
+  // partial last column tile) load row N - 1.
   const int src_first = rowsrc[0];
-  const uint8_t *asrc[8];
-  const uint8_t *bsrc[8];
+  const uint8_t *asrc[2];
+  const uint8_t *bsrc[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = wave * 32 + hh * 16 + (lane >> 2);
+    const int ch = (lane & 3) ^ ((row >> 2) & 3);
     const int src = rowsrc[row] >= 0 ? rowsrc[row] : src_first;
-    asrc[i] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
-    const uint8_t *base;
-    int n;
-    if (SWIGLU) {
-      base = row < kBW / 2 ? B0 : B1;
-      n = n0 + (row & (kBW / 2 - 1));
-    } else {
-      base = B0;
-      n = n0 + row;
-    }
-    bsrc[i] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16;
+    asrc[hh] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
+    const int n = n0 + (SWIGLU ? (row & (kBW / 2 - 1)) : row);
+    const uint8_t *base = (SWIGLU && row >= kBW / 2) ? B1 : B0;
+    bsrc[hh] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16;
   }
-  u32x4 ra[8], rb[8];
-  // slots are moved in 4 parts of 2 (A) + 2 (B) so that LDS stores and
-  // global loads interleave with the 4 MFMA k-steps of a stage
-  auto gload_part = [&](int part, int s) {
+  auto issue = [&](int s) {  // stage s -> ring slot s % kRing
+    uint8_t *slot = lds + (s % kRing) * kSlot;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) {
-      ra[i] = ld16(asrc[i] + static_cast<int64_t>(s) * kRow);
-      rb[i] = ld16(bsrc[i] + static_cast<int64_t>(s) * kRow);
-    }
-  };
-  auto lstore_part = [&](int part, int buf) {
-#pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      st16(ldsA + buf * kBM * kRow + swz(row, ch), ra[i]);
-      st16(ldsB + buf * kBW * kRow + swz(row, ch), rb[i]);
+    for (int hh = 0; hh < 2; ++hh) {
+      dma16(asrc[hh] + static_cast<int64_t>(s) * kStage, slot + (wave * 2 + hh) * 1024);
+      dma16(bsrc[hh] + static_cast<int64_t>(s) * kStage,
+            slot + kBM * kStage + (wave * 2 + hh) * 1024);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
+    for (int n = 0; n < 2; ++n) acc[m][n] = f32x16{};
 
-  // weight rows of n-block n for this wave
-  int wrow[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n)
-    wrow[n] = SWIGLU ? ((n >> 1) * (kBW / 2) + wc * 64 + (n & 1) * 32 + r32)
-                     : (wc * 128 + n * 32 + r32);
+  // weight rows of this wave: gate/up -> gate block (wc * 32) and the up
+  // block at the same columns (128 + wc * 32); down -> wc * 64 + {0, 32}
+  const int wrow0 = SWIGLU ? wc * 32 + r32 : wc * 64 + r32;
+  const int wrow1 = SWIGLU ? kBW / 2 + wc * 32 + r32 : wc * 64 + 32 + r32;
 
+  // prologue: stages 0 .. kRing-2 in flight
 #pragma unroll
-  for (int part = 0; part < 4; ++part) gload_part(part, 0);
-#pragma unroll
-  for (int part = 0; part < 4; ++part) lstore_part(part, 0);
-  if (nst > 1) {
-#pragma unroll
-    for (int part = 0; part < 4; ++part) gload_part(part, 1);
-  }
-  __syncthreads();
+  for (int s = 0; s < kRing - 1; ++s)
+    if (s < nst) issue(s);
   for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    const uint8_t *la = ldsA + buf * kBM * kRow;
-    const uint8_t *lb = ldsB + buf * kBW * kRow;
-    const bool more = s + 1 < nst, more2 = s + 2 < nst;
+    // this wave's loads of stage s are done when at most the loads of the
+    // later stages already issued (4 per stage) are outstanding; the
+    // barrier then covers every wave's loads, and also guarantees that all
+    // waves finished reading the slot the next issue overwrites
+    const int later = min(kRing - 2, nst - 1 - s);
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (s + kRing - 1 < nst) issue(s + kRing - 1);
+    const uint8_t *la = lds + (s % kRing) * kSlot;
+    const uint8_t *lb = la + kBM * kStage;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       const int ch = 2 * ks + g;
-      bf16x8 bfr[4], afr[4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) bfr[n] = bitcast<bf16x8>(ld16(lb + swz(wrow[n], ch)));
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        afr[m] = bitcast<bf16x8>(ld16(la + swz(wr * 128 + m * 32 + r32, ch)));
+      bf16x8 fa[4], fb[2];
+      fb[0] = bitcast<bf16x8>(ld16(lb + swz64(wrow0, ch)));
+      fb[1] = bitcast<bf16x8>(ld16(lb + swz64(wrow1, ch)));
 #pragma unroll
       for (int m = 0; m < 4; ++m)
+        fa[m] = bitcast<bf16x8>(ld16(la + swz64(wr * 128 + m * 32 + r32, ch)));
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[m], bfr[n], acc[m][n], 0, 0, 0);
-      // stage s+1 (loaded during the previous stage) into the other buffer,
-      // then reuse the registers for stage s+2
-      if (more) {
-        lstore_part(ks, buf ^ 1);
-        if (more2) gload_part(ks, s + 2);
-      }
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
     }
-    __syncthreads();
   }
+  __syncthreads();  // all waves are done with the ring before the epilogue reuses it
 
   // ---- epilogue: stage the bf16 tile in LDS, then whole 16-byte stores.
   // acc[m][n][i]: row 32 m + 8 (i / 4) + 4 g + (i % 4), column r32 of block n.
@@ -189,24 +186,18 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
     for (int i = 0; i < 16; ++i) {
       const int row = wr * 128 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
       if (SWIGLU) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int col = wc * 64 + jj * 32 + r32;
-          o16[row * OPITCH + col] = f32_to_bf16(silu_mul(acc[m][jj][i], acc[m][2 + jj][i]));
-        }
+        o16[row * OPITCH + wc * 32 + r32] = f32_to_bf16(silu_mul(acc[m][0][i], acc[m][1][i]));
       } else {
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const int col = wc * 128 + n * 32 + r32;
-          o16[row * OPITCH + col] = f32_to_bf16(acc[m][n][i]);
-        }
+        for (int n = 0; n < 2; ++n)
+          o16[row * OPITCH + wc * 64 + n * 32 + r32] = f32_to_bf16(acc[m][n][i]);
       }
     }
   }
   __syncthreads();
   constexpr int CPR = OPITCH * 2 / 16;  // 16-byte pieces per staged row
   const int vcpr = min(CPR, (N - n0) * 2 / 16);
-  for (int c = tid; c < kBM * CPR; c += 256) {
+  for (int c = tid; c < kBM * CPR; c += 512) {
     const int row = c / CPR, col = c % CPR;
     if (row < rows && col < vcpr)
       st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
@@ -217,7 +208,7 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(const GemmArgs p) {
 template <bool SWIGLU>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
-  constexpr size_t kLds = 2 * (kBM + kBW) * kRow;  // 128 KB
+  constexpr size_t kLds = kRing * kSlot;  // 128 KB
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_gemm_kernel<SWIGLU>),
@@ -229,7 +220,7 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   const int ntn = (nmax + BNO - 1) / BNO;
   const int64_t grid = 8LL * ((a.tiles_ub + 7) / 8) * ntn;
   if (grid <= 0) return hipSuccess;
-  prefill_gemm_kernel<SWIGLU><<<static_cast<unsigned>(grid), 256, kLds, s>>>(a);
+  prefill_gemm_kernel<SWIGLU><<<static_cast<unsigned>(grid), 512, kLds, s>>>(a);
   return hipGetLastError();
 }
 
