@@ -63,6 +63,7 @@ struct afd_ffn_handle {
   float *xs;
   uint8_t *z;
   float *zs;
+  float *z32;  // W8A8 with the streaming kernels: fp32 z before quantisation
   uint8_t *y;
   // profiling
   uint32_t prof_mask;
@@ -214,6 +215,8 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
     parts.push_back({reinterpret_cast<void **>(&h->xs), sizeof(float) * T * (hd / 128)});
     parts.push_back(
         {reinterpret_cast<void **>(&h->zs), sizeof(float) * R * (h->zpitch / 128)});
+    parts.push_back(
+        {reinterpret_cast<void **>(&h->z32), sizeof(float) * R * h->zpitch});
   }
   size_t total = 0;
   for (auto &p : parts) total = align_up(total, 256) + align_up(p.bytes, 256);
@@ -365,10 +368,33 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   g.c_pitch = static_cast<int64_t>(h->zpitch) * zes;
   g.c_scale = h->zs;
   g.c_scale_pitch = h->zpitch / 128;
+  // W8A8 on the streaming kernels: gate/up writes fp32 z, then the 1x128
+  // quantiser produces the E4M3 rows and scales the down GEMM reads
+  const bool z_fp32 = h->elem == 2 && plan.small_kernel == afd::GemmKernel::Stream;
+  if (z_fp32) {
+    g.C = reinterpret_cast<uint8_t *>(h->z32);
+    g.c_pitch = static_cast<int64_t>(h->zpitch) * 4;
+  }
   ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
   e = launch_gemms(h, afd::GemmKind::GateUp, plan, g, T, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
+  if (z_fp32) {
+    ev = prof_begin(h, AFD_STAGE_QUANT, s);
+    const int64_t R = static_cast<int64_t>(Tk) + static_cast<int64_t>(S) * Ti;
+    // routed rows have I columns; shared rows I_s (quantised in two calls
+    // when the widths differ)
+    e = afd::launch_quant_1x128_f32(h->z32, Tk, c.inter, h->zpitch, h->z, h->zpitch, h->zs,
+                                    h->zpitch / 128, s);
+    if (e == hipSuccess && S > 0)
+      e = afd::launch_quant_1x128_f32(h->z32 + static_cast<int64_t>(Tk) * h->zpitch, R - Tk,
+                                      c.shared_inter, h->zpitch,
+                                      h->z + static_cast<int64_t>(Tk) * h->zpitch, h->zpitch,
+                                      h->zs + static_cast<int64_t>(Tk) * (h->zpitch / 128),
+                                      h->zpitch / 128, s);
+    prof_end(ev, s);
+    if (e != hipSuccess) return hip_fail(e, "z quantiser launch");
+  }
 
   afd::GemmArgs d = g;
   d.A = h->z;

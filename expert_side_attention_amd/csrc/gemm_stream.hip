@@ -24,7 +24,7 @@
 //    A and B use the same byte->K assignment, so the products are exact
 //    permutations of the K sum.
 //  * Epilogues stage the tile through LDS and write whole 16-byte pieces;
-//    the fp8 gate/up epilogue quantises z per row per 128 columns.
+//    the fp8 gate/up epilogue writes z in fp32 for the 1x128 quantiser.
 #include "common.h"
 #include <type_traits>
 
@@ -55,11 +55,11 @@ struct StreamCfg {
   static constexpr bool FP8 = EL == Elem::FP8;
   static constexpr int LDS_A = 2 * BM * APITCH;
   // epilogue staging: BM rows x BN columns of the output element
-  static constexpr int OUT_ES = FP8 && SWIGLU ? 1 : 2;
+  static constexpr int OUT_ES = FP8 && SWIGLU ? 4 : 2;  // fp32 z (W8A8) or bf16
   static constexpr int LDS_OUT = BM * BN * OUT_ES;
   static constexpr int LDS = LDS_A > LDS_OUT ? LDS_A : LDS_OUT;
   static_assert(BM % 16 == 0 && SS % 128 == 0, "shape");
-  static_assert(!FP8 || BN == 128, "fp8: one weight scale block row per item");
+  static_assert(!FP8 || 128 % BN == 0, "fp8: an item lies inside one weight scale block row");
 };
 
 template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
@@ -72,7 +72,6 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
   __shared__ __align__(16) uint8_t lds[C::LDS];
   __shared__ int rowsrc[BM];
   __shared__ float sAs[2][C::FP8 ? BM * KB : 1];
-  __shared__ float red[C::FP8 && SWIGLU ? WAVES * BM : 1];
   __shared__ int s_item;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -277,37 +276,23 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
 
     // ---- epilogue (A buffers are free: every wave passed the last barrier)
     if constexpr (SWIGLU && C::FP8) {
-      float zv[MB][4];
-#pragma unroll
-      for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          zv[b][i] = silu_mul(acc[0][b][i], acc[1][b][i]);
-          const float mx = group16_max(fabsf(zv[b][i]));
-          if (r16 == 0) red[wave * BM + b * 16 + q * 4 + i] = mx;
-        }
-      __syncthreads();
-      // per-row scale; codes staged as [BM][128] bytes
+      // W8A8: z = silu(g) * u stays fp32 here; the 1x128 quantiser runs on
+      // it afterwards (a quantisation group spans two items of 64 columns)
+      float *o32 = reinterpret_cast<float *>(lds);
 #pragma unroll
       for (int b = 0; b < MB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = b * 16 + q * 4 + i;
-          float amax = 0.0f;
-#pragma unroll
-          for (int w = 0; w < WAVES; ++w) amax = fmaxf(amax, red[w * BM + row]);
-          const float sc = e4m3_scale(amax);
-          lds[row * BN + wave * 16 + r16] = static_cast<uint8_t>(f32_to_e4m3(zv[b][i] / sc));
-          if (wave == 0 && r16 == 0 && row < rows)
-            p.c_scale[static_cast<int64_t>(tile.row0 + row) * p.c_scale_pitch + n0 / 128] = sc;
+          o32[row * BN + wave * 16 + r16] = silu_mul(acc[0][b][i], acc[1][b][i]);
         }
       __syncthreads();
-      constexpr int PIECES = BM * BN / 16;
+      constexpr int PIECES = BM * BN * 4 / 16;
       for (int c = tid; c < PIECES; c += THREADS) {
-        const int row = c / (BN / 16), col = c % (BN / 16);
+        const int row = c / (BN * 4 / 16), col = c % (BN * 4 / 16);
         if (row < rows)
-          st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 + col * 16,
-               ld16(lds + row * BN + col * 16));
+          st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 4 + col * 16,
+               ld16(lds + row * BN * 4 + col * 16));
       }
     } else {
       uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
@@ -347,6 +332,7 @@ hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
   constexpr int BN = 16 * WAVES;
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int64_t items = static_cast<int64_t>(a.tiles_ub) * (nmax / BN);
+  // persistent: one resident wave of workgroups
   int64_t grid = static_cast<int64_t>(cus) * per_cu;
   if (items < grid) grid = items;
   if (grid <= 0) return hipSuccess;
@@ -368,11 +354,11 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
                 : launch_stream<Elem::BF16, 8, 128, 256, false>(a, s);
   } else if (elem == 2) {
     if (bm == 64)
-      return gu ? launch_stream<Elem::FP8, 8, 64, 256, true>(a, s)
-                : launch_stream<Elem::FP8, 8, 64, 256, false>(a, s);
+      return gu ? launch_stream<Elem::FP8, 4, 64, 512, true>(a, s)
+                : launch_stream<Elem::FP8, 4, 64, 512, false>(a, s);
     if (bm == 128)
-      return gu ? launch_stream<Elem::FP8, 8, 128, 256, true>(a, s)
-                : launch_stream<Elem::FP8, 8, 128, 256, false>(a, s);
+      return gu ? launch_stream<Elem::FP8, 4, 128, 256, true>(a, s)
+                : launch_stream<Elem::FP8, 4, 128, 256, false>(a, s);
   }
   return hipErrorInvalidValue;
 }

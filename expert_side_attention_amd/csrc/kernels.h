@@ -48,6 +48,10 @@ hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
 
 hipError_t launch_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
                               uint8_t *q, float *sc, hipStream_t s);
+// fp32 rows with pitches (elements / bytes / floats) for x, q and scales.
+hipError_t launch_quant_1x128_f32(const float *x, int64_t rows, int64_t cols, int64_t pitch,
+                                  uint8_t *q, int64_t qpitch, float *sc, int64_t spitch,
+                                  hipStream_t s);
 hipError_t launch_quant_128x128(const uint16_t *w, int64_t rows,
                                 int64_t cols, uint8_t *q, float *sc,
                                 hipStream_t s);

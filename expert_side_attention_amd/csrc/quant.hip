@@ -42,6 +42,42 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(
   if (sub == 0) sc[row * groups_per_row + cg] = s;
 }
 
+// The same quantiser on fp32 input (z of the W8A8 gate/up GEMM): 16 lanes
+// per 128-column group, 8 floats (two 16-byte loads) per lane.  Rows have a
+// pitch of `pitch` floats (>= cols); codes use pitch `qpitch` bytes, scales
+// `spitch` floats.
+__global__ __launch_bounds__(256) void quant_1x128_f32_kernel(
+    const float *__restrict__ x, int64_t rows, int64_t cols, int64_t pitch,
+    uint8_t *__restrict__ q, int64_t qpitch, float *__restrict__ sc, int64_t spitch) {
+  const int64_t groups_per_row = cols / 128;
+  const int64_t g = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 4;
+  if (g >= rows * groups_per_row) return;  // uniform over the 16-lane group
+  const int sub = threadIdx.x & 15;
+  const int64_t row = g / groups_per_row, cg = g % groups_per_row;
+  const float *src = x + row * pitch + cg * 128 + sub * 8;
+  const u32x4 v0 = ld16(src), v1 = ld16(src + 4);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = __uint_as_float(v0[i]);
+    f[4 + i] = __uint_as_float(v1[i]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = group16_max(amax);
+  const float s = e4m3_scale(amax);
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w0 |= f32_to_e4m3(f[i] / s) << (8 * i);
+    w1 |= f32_to_e4m3(f[4 + i] / s) << (8 * i);
+  }
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2 *>(q + row * qpitch + cg * 128 + sub * 8) = u32x2{w0, w1};
+  if (sub == 0) sc[row * spitch + cg] = s;
+}
+
 // One workgroup per 128x128 block; thread = (row tid/2, 64-column half).
 __global__ __launch_bounds__(256) void quant_128x128_kernel(
     const uint16_t *__restrict__ w, int64_t rows, int64_t cols,
@@ -95,6 +131,16 @@ hipError_t launch_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
   const int64_t groups = rows * (cols / 128);
   const int64_t blocks = (groups * 16 + 255) / 256;
   quant_1x128_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(x, rows, cols, q, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_1x128_f32(const float *x, int64_t rows, int64_t cols, int64_t pitch,
+                                  uint8_t *q, int64_t qpitch, float *sc, int64_t spitch,
+                                  hipStream_t s) {
+  const int64_t groups = rows * (cols / 128);
+  const int64_t blocks = (groups * 16 + 255) / 256;
+  quant_1x128_f32_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(x, rows, cols, pitch, q,
+                                                                        qpitch, sc, spitch);
   return hipGetLastError();
 }
 
