@@ -56,7 +56,7 @@ struct afd_ffn_handle {
   void *ws;
   size_t ws_bytes;
   int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *num_big, *counters;
-  int32_t *router_counters;
+  int32_t *router_counters, *dispatch_scratch;
   float *topk_w, *logits;
   afd::Tile *tiles, *tiles_big;
   uint8_t *xq;
@@ -204,6 +204,8 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
       {reinterpret_cast<void **>(&h->num_big), sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->counters), 2 * sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->router_counters), sizeof(int32_t) * afd::router_blocks(T)},
+      {reinterpret_cast<void **>(&h->dispatch_scratch),
+       sizeof(int32_t) * 2 * afd::dispatch_blocks(static_cast<int>(T)) * E},
       {reinterpret_cast<void **>(&h->logits), sizeof(float) * T * E},
       {reinterpret_cast<void **>(&h->tiles), sizeof(afd::Tile) * h->tiles_cap},
       {reinterpret_cast<void **>(&h->tiles_big), sizeof(afd::Tile) * h->big_cap},
@@ -325,7 +327,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   ev = prof_begin(h, AFD_STAGE_DISPATCH, s);
   e = afd::launch_dispatch(h->ids, Ti, k, E, S, plan.tiles, h->counts, h->offsets, h->perm,
                            h->slot_row, h->tiles, h->num_tiles, h->tiles_big, h->num_big,
-                           h->counters, 2, s);
+                           h->counters, 2, h->dispatch_scratch, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
 

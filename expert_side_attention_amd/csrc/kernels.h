@@ -40,11 +40,14 @@ struct TilePlan {
 // Histogram, scan and stable scatter of the (token, slot) pairs, and the
 // two GEMM tile lists (routed experts, then the S shared groups).  Also
 // zeroes `counters[0..ncounters)` (the GEMMs' work counters).
+// block_scratch: 2 * dispatch_blocks(T) * E int32 (used when T > 1024).
+int dispatch_blocks(int T);
 hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
                            const TilePlan &tp, int32_t *counts, int32_t *offsets,
                            int32_t *perm, int32_t *slot_row, Tile *tiles_s,
                            int32_t *num_s, Tile *tiles_b, int32_t *num_b,
-                           int32_t *counters, int ncounters, hipStream_t s);
+                           int32_t *counters, int ncounters, int32_t *block_scratch,
+                           hipStream_t s);
 
 hipError_t launch_quant_1x128(const uint16_t *x, int64_t rows, int64_t cols,
                               uint8_t *q, float *sc, hipStream_t s);

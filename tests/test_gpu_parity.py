@@ -70,6 +70,8 @@ SMALL = [
     LayerShape("bf16_zipf", T=500, h=256, E=32, k=4, I=128, S=1, Is=128, mode="bf16",
                router="zipf"),
     LayerShape("bf16_big_t", T=2100, h=128, E=64, k=2, I=128, mode="bf16"),
+    LayerShape("bf16_e512_blocks", T=2049, h=128, E=512, k=8, I=128, S=1, Is=128,
+               mode="bf16"),
     LayerShape("f32_k_eq_e", T=70, h=128, E=4, k=4, I=128, S=1, Is=256, mode="f32"),
     LayerShape("w8a8_small", T=200, h=512, E=8, k=2, I=256, S=1, Is=384, mode="w8a8"),
     LayerShape("w8a8_many", T=96, h=256, E=32, k=8, I=384, mode="w8a8"),
