@@ -56,7 +56,7 @@ struct afd_ffn_handle {
   void *ws;
   size_t ws_bytes;
   int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *num_big, *counters;
-  int32_t *router_counters, *dispatch_scratch;
+  int32_t *dispatch_scratch;
   float *topk_w, *logits;
   afd::Tile *tiles, *tiles_big;
   uint8_t *xq;
@@ -203,7 +203,6 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
       {reinterpret_cast<void **>(&h->num_tiles), sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->num_big), sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->counters), 2 * sizeof(int32_t)},
-      {reinterpret_cast<void **>(&h->router_counters), sizeof(int32_t) * afd::router_blocks(T)},
       {reinterpret_cast<void **>(&h->dispatch_scratch),
        sizeof(int32_t) * 2 * afd::dispatch_blocks(static_cast<int>(T)) * E},
       {reinterpret_cast<void **>(&h->logits), sizeof(float) * T * E},
@@ -234,15 +233,6 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
     off = align_up(off, 256);
     *p.dst = static_cast<char *>(h->ws) + off;
     off += align_up(p.bytes, 256);
-  }
-  // the router's completion counters start at zero; every forward leaves
-  // them at zero again
-  e = hipMemset(h->router_counters, 0, sizeof(int32_t) * afd::router_blocks(T));
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess) {
-    hipFree(h->ws);
-    delete h;
-    return hip_fail(e, "workspace initialisation");
   }
   *out = h;
   return AFD_OK;
@@ -319,7 +309,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   ev = prof_begin(h, AFD_STAGE_ROUTER, s);
   e = afd::launch_router(h->elem == 0, hidden, h->w.router_w,
                          c.has_router_bias ? h->w.router_b : nullptr, Ti, hd, E, k, h->logits,
-                         h->router_counters, h->ids, h->topk_w, s);
+                         h->ids, h->topk_w, s);
   prof_end(ev, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
 

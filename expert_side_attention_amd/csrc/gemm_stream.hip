@@ -348,7 +348,7 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
   if (elem == 1) {
     if (bm == 64)
       return gu ? launch_stream<Elem::BF16, 4, 64, 512, true>(a, s)
-                : launch_stream<Elem::BF16, 8, 64, 512, false>(a, s);
+                : launch_stream<Elem::BF16, 8, 64, 128, false>(a, s);
     if (bm == 128)
       return gu ? launch_stream<Elem::BF16, 4, 128, 256, true>(a, s)
                 : launch_stream<Elem::BF16, 8, 128, 256, false>(a, s);

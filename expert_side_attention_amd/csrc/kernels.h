@@ -21,13 +21,10 @@ constexpr int kMaxShared = 8;
 
 // Router GEMM + softmax + top-k + renormalisation.
 // f32: x, wr are fp32; else bf16.  bias may be null.  bf16 path scratch:
-// logits [T, E] fp32 and counters [router_blocks(T)] int32, which must be
-// zero before the first call and are left zero by every call.
-int router_blocks(int T);
+// logits [T, E] fp32.
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
-                         float *logits, int32_t *counters, int32_t *ids, float *w,
-                         hipStream_t s);
+                         float *logits, int32_t *ids, float *w, hipStream_t s);
 
 // Row-tile lists of a forward: small tiles (bm_small rows) and, if
 // bm_big > 0, big tiles (bm_big rows) for groups of at least big_min rows.

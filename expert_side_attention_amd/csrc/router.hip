@@ -36,11 +36,11 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
   return x;
 }
 
-// Top-k over the logits of TM tokens held in LDS (row pitch E), one wave per
-// token at a time.  NC = candidates per lane (E <= 64 * NC).
+// Top-k over the logits of TM tokens (row pitch E, in LDS or global memory),
+// one wave per token at a time.  NC = candidates per lane (E <= 64 * NC).
 template <int TM, int NC, int WAVES = 4>
-__device__ void topk_from_lds(const float *sl, float *selv, int t0, int T,
-                              int E, int k, int32_t *ids, float *wout) {
+__device__ void topk_rows(const float *sl, float *selv, int t0, int T,
+                          int E, int k, int32_t *ids, float *wout) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   float *mysel = selv + wave * kMaxExperts;
@@ -81,28 +81,21 @@ __device__ void topk_from_lds(const float *sl, float *selv, int t0, int T,
   }
 }
 
-// bf16 router.  The grid is (expert slices of EN) x (token blocks of TM), so
-// even small batches spread over many CUs.  Inside a workgroup the WAVES
-// waves take disjoint slices of h and compute all TM x EN partial logits with
-// operands loaded straight from global memory into MFMA registers (no LDS,
-// no barrier in the K loop, NBUF chunks of prefetch); the partial sums are
-// added in wave order, so the logits do not depend on timing.  Each
-// workgroup stores its logit slice; the last one to finish a token block
-// (device-scope counter) runs the top-k for that block and resets the
-// counter to 0 for the next call.  EMAX bounds E (top-k LDS size).
-template <int TM, int EN, int NBUF, int WAVES, int EMAX>
+// bf16 router logits.  The grid is (expert slices of EN) x (token blocks of
+// TM), so even small batches spread over many CUs.  Inside a workgroup the
+// WAVES waves take disjoint slices of h and compute all TM x EN partial
+// logits with operands loaded straight from global memory into MFMA
+// registers (no LDS, no barrier in the K loop, NBUF chunks of prefetch); the
+// partial sums are added in wave order, so the logits do not depend on
+// timing.  The top-k runs in the next kernel: a device-wide hand-over inside
+// this one would need an L2 write-back and invalidate per workgroup.
+template <int TM, int EN, int NBUF, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void router_bf16_kernel(
     const uint16_t *__restrict__ X, const uint16_t *__restrict__ Wr,
-    const float *__restrict__ bias, int T, int h, int E, int k,
-    float *__restrict__ logits, int32_t *__restrict__ counters,
-    int32_t *__restrict__ ids, float *__restrict__ wout) {
+    const float *__restrict__ bias, int T, int h, int E, float *__restrict__ logits) {
   constexpr int MB = TM / 16, NB = EN / 16;
   constexpr int THREADS = WAVES * 64;
-  constexpr int RED = WAVES * TM * EN;
-  constexpr int TOPK = TM * EMAX;
-  __shared__ float red[RED > TOPK ? RED : TOPK];
-  __shared__ float selv[WAVES * kMaxExperts];
-  __shared__ int is_last;
+  __shared__ float red[WAVES * TM * EN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, r16 = lane & 15;
@@ -181,25 +174,16 @@ __global__ __launch_bounds__(WAVES * 64) void router_bf16_kernel(
       logits[static_cast<int64_t>(t) * E + e] = v;
     }
   }
-  __threadfence();  // this slice's logits are visible device-wide before the count
-  __syncthreads();
-  if (tid == 0) {
-    const int done = atomicAdd(&counters[blockIdx.y], 1);
-    is_last = done == static_cast<int>(gridDim.x) - 1;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (tid == 0) counters[blockIdx.y] = 0;
-  for (int i = tid; i < TM * E; i += THREADS) {
-    const int tt = i / E, e = i % E;
-    const int t = t0 + tt;
-    red[i] = t < T ? __hip_atomic_load(&logits[static_cast<int64_t>(t) * E + e], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)
-                   : 0.0f;
-  }
-  __syncthreads();
-  topk_from_lds<TM, EMAX / 64, WAVES>(red, selv, t0, T, E, k, ids, wout);
+}
+
+// Top-k and weights from the logits: one wave per token, four per workgroup.
+template <int NC>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T,
+                                                   int E, int k, int32_t *__restrict__ ids,
+                                                   float *__restrict__ wout) {
+  __shared__ float selv[4 * kMaxExperts];
+  const int t0 = blockIdx.x * 4;
+  topk_rows<4, NC, 4>(logits + static_cast<int64_t>(t0) * E, selv, t0, T, E, k, ids, wout);
 }
 
 // fp32 router for small layers: one (token, expert) dot product per thread.
@@ -223,17 +207,15 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
     sl[tt * E + e] = a;
   }
   __syncthreads();
-  topk_from_lds<TM, kMaxExperts / 64>(sl, selv, t0, T, E, k, ids, wout);
+  topk_rows<TM, kMaxExperts / 64>(sl, selv, t0, T, E, k, ids, wout);
 }
 
 }  // namespace
 
-int router_blocks(int T) { return (T + 15) / 16; }
-
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
-                         float *logits, int32_t *counters, int32_t *ids, float *w,
-                         hipStream_t s) {
+                         float *logits, int32_t *ids, float *w, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
   if (f32) {
     constexpr int TM = 16;
     router_f32_kernel<TM><<<(T + TM - 1) / TM, 256, 0, s>>>(
@@ -246,29 +228,35 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   // token blocks of 16 (64 for long batches), expert slices sized so that a
   // batch launches a few hundred workgroups, K split over 8 waves (4 for the
   // 64-token blocks, whose partial sums would not fit LDS otherwise)
-#define AFD_ROUTER(TM, EN, NBUF, WAVES, EMAX)                                          \
-  router_bf16_kernel<TM, EN, NBUF, WAVES, EMAX>                                       \
-      <<<dim3((E + EN - 1) / EN, (T + TM - 1) / TM), WAVES * 64, 0, s>>>(             \
-          X, W, bias, T, h, E, k, logits, counters, ids, w)
+#define AFD_ROUTER(TM, EN, NBUF, WAVES)                                                 \
+  router_bf16_kernel<TM, EN, NBUF, WAVES>                                              \
+      <<<dim3((E + EN - 1) / EN, (T + TM - 1) / TM), WAVES * 64, 0, s>>>(X, W, bias, T, h, \
+                                                                           E, logits)
   // each wave's K slice must be whole 32-element chunks: 8 waves need
   // h % 256 == 0, 4 waves h % 128 == 0 (always true here)
   const bool k8 = h % 256 == 0;
   if (E > 256) {
-    if (k8) AFD_ROUTER(16, 64, 4, 8, 512);
-    else AFD_ROUTER(16, 64, 4, 4, 512);
+    if (k8) AFD_ROUTER(16, 64, 4, 8);
+    else AFD_ROUTER(16, 64, 4, 4);
   } else if (T > 4096) {
-    AFD_ROUTER(64, 64, 4, 4, 256);
+    AFD_ROUTER(64, 64, 4, 4);
   } else if (E <= 64 || T <= 256) {
-    if (k8) AFD_ROUTER(16, 16, 8, 8, 256);
-    else AFD_ROUTER(16, 16, 8, 4, 256);
+    if (k8) AFD_ROUTER(16, 16, 8, 8);
+    else AFD_ROUTER(16, 16, 8, 4);
   } else if (T <= 1024) {
-    if (k8) AFD_ROUTER(16, 32, 6, 8, 256);
-    else AFD_ROUTER(16, 32, 6, 4, 256);
+    if (k8) AFD_ROUTER(16, 32, 6, 8);
+    else AFD_ROUTER(16, 32, 6, 4);
   } else {
-    if (k8) AFD_ROUTER(16, 64, 4, 8, 256);
-    else AFD_ROUTER(16, 64, 4, 4, 256);
+    if (k8) AFD_ROUTER(16, 64, 4, 8);
+    else AFD_ROUTER(16, 64, 4, 4);
   }
 #undef AFD_ROUTER
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
+  if (E <= 64) topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 256) topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w);
+  else topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w);
   return hipGetLastError();
 }
 
