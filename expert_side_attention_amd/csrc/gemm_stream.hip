@@ -46,11 +46,11 @@ struct StreamCfg {
   static constexpr int NMAT = SWIGLU ? 2 : 1;
   static constexpr int BN = 16 * WAVES;       // columns per matrix per item
   static constexpr int MB = BM / 16;
-  static constexpr int NCH = SS / 64;         // 16-byte chunks per lane per row block
-  static constexpr int NPR = NCH / 2;         // chunk pairs (one fp8 K block each)
+  static constexpr int NPR = SS / 128;        // 128-byte K pieces per row per super-stage
   static constexpr int APITCH = SS + 16;      // LDS row pitch of the A stage
-  static constexpr int ACH = BM * SS / 16;    // 16-byte chunks of one A stage
-  static constexpr int RA = (ACH + kThreads - 1) / kThreads;
+  static constexpr int CPR = SS / 16;         // 16-byte chunks of one A row per super-stage
+  static constexpr int RPP = kThreads / CPR;  // A rows staged per pass of the workgroup
+  static constexpr int RA = BM / RPP;         // passes
   static constexpr int KB = SS / 128;         // fp8 scale blocks per super-stage
   static constexpr bool FP8 = EL == Elem::FP8;
   static constexpr int LDS_A = 2 * BM * APITCH;
@@ -59,18 +59,21 @@ struct StreamCfg {
   static constexpr int LDS_OUT = BM * BN * OUT_ES;
   static constexpr int LDS = LDS_A > LDS_OUT ? LDS_A : LDS_OUT;
   static_assert(BM % 16 == 0 && SS % 128 == 0, "shape");
+  static_assert(kThreads % CPR == 0 && BM % RPP == 0, "A staging passes");
   static_assert(!FP8 || 128 % BN == 0, "fp8: an item lies inside one weight scale block row");
+  static_assert(!FP8 || BM * KB <= kThreads, "fp8: one activation scale per thread");
 };
 
+// K (in bytes per row) must be a multiple of SS for every group; the
+// launcher picks an instantiation that satisfies this, so the main loop has
+// no partial super-stage and no per-load guard.
 template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
-__global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs p) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void stream_gemm_kernel(const GemmArgs p) {
   using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU>;
-  constexpr int NMAT = C::NMAT, BN = C::BN, MB = C::MB, NCH = C::NCH;
-  constexpr int APITCH = C::APITCH, ACH = C::ACH, RA = C::RA, KB = C::KB;
-  constexpr int THREADS = C::kThreads;
+  constexpr int NMAT = C::NMAT, BN = C::BN, MB = C::MB, NPR = C::NPR;
+  constexpr int APITCH = C::APITCH, CPR = C::CPR, RPP = C::RPP, RA = C::RA, KB = C::KB;
 
   __shared__ __align__(16) uint8_t lds[C::LDS];
-  __shared__ int rowsrc[BM];
   __shared__ float sAs[2][C::FP8 ? BM * KB : 1];
   __shared__ int s_item;
 
@@ -78,13 +81,15 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
   const int q = lane >> 4, r16 = lane & 15;
   const int nmax = p.N > p.Ns ? p.N : p.Ns;
   const int ntn = nmax / BN;
+  const int total = *p.num_tiles * ntn;
+  const int acol = tid % CPR, arow0 = tid / CPR;  // this thread's A chunk column, first row
+  constexpr int ES = C::FP8 ? 1 : 2;
 
   for (;;) {
     __syncthreads();  // every thread has read the previous s_item
     if (tid == 0) s_item = atomicAdd(p.work_counter, 1);
     __syncthreads();
-    const int item = s_item;
-    const int total = *p.num_tiles * ntn;
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= total) break;
     const Tile tile = p.tiles[item / ntn];
     const int nt = item % ntn;
@@ -95,25 +100,28 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
     if (n0 >= N) continue;  // uniform over the workgroup
     const int g = shared ? tile.group - p.E : tile.group;
     const int rows = tile.rows;
-    if (tid < BM) {
-      int src = -1;
-      if (tid < rows) {
-        const int r = tile.row0 + tid;
-        src = p.perm ? (r < p.Tk ? p.perm[r] : (r - p.Tk) % p.T) : r;
-      }
-      rowsrc[tid] = src;
-    }
-    __syncthreads();
+    const int64_t krow = static_cast<int64_t>(K) * ES;
+    const int nss = static_cast<int>(krow / SS);
 
-    const int ES = C::FP8 ? 1 : 2;
-    const int64_t krow = static_cast<int64_t>(K) * ES;  // a multiple of 128
-    // the last super-stage may be partial: it holds `valid_pairs` 128-byte
-    // K pieces; nothing beyond a row's end is ever read
-    const int nss = static_cast<int>((krow + SS - 1) / SS);
-    auto valid_pairs = [&](int ss) {
-      const int64_t left = (krow - static_cast<int64_t>(ss) * SS) / 128;
-      return left < C::NPR ? static_cast<int>(left) : C::NPR;
+    // A rows this thread stages; rows past the tile's end repeat its first
+    // row (they only feed output rows that are never stored)
+    auto source_row = [&](int row) {
+      const int r = tile.row0 + (row < rows ? row : 0);
+      return p.perm ? (r < p.Tk ? p.perm[r] : (r - p.Tk) % p.T) : r;
     };
+    int asrc[RA];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) asrc[i] = source_row(arow0 + i * RPP);
+    const uint8_t *abase_g = p.A + acol * 16;
+    // activation scales: thread tid < BM * KB stages scale (row tid / KB,
+    // block tid % KB); the others load a valid address and drop the value,
+    // so every load of the main loop is unconditional
+    const float *asc = p.a_scale;
+    if constexpr (C::FP8) {
+      const int as_t = tid < BM * KB ? tid : 0;
+      asc = p.a_scale + static_cast<int64_t>(source_row(as_t / KB)) * p.a_scale_pitch + as_t % KB;
+    }
+
     const int64_t mat = static_cast<int64_t>(N) * krow;
     const uint8_t *bptr[NMAT];
     {
@@ -133,58 +141,43 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
     }
     const int mb_active = (rows + 15) >> 4;
 
-    // ---- register buffers: chunk pairs (2c, 2c+1) share one 8-dword
-    // register tuple, which is exactly one fp8 MFMA operand
-    u32x8 bq[2][NMAT][C::NPR];
+    // ---- registers: 128-byte K piece c of a row block is one 8-dword tuple
+    // (bytes [128 c + 16 q] and [128 c + 64 + 16 q]), one fp8 MFMA operand or
+    // two bf16 MFMA operands
+    u32x8 bq[2][NMAT][NPR];
+    float sbq[2][NMAT][C::FP8 ? KB : 1];
     u32x4 ra[RA];
     float as_reg = 0.0f;
-    auto load_b = [&](u32x8 (&dst)[NMAT][C::NPR], int ss) {
-      const int vp = valid_pairs(ss);
+    // order of issue per super-stage: A rows, A scales, B scales, B rows.
+    // Vector loads complete in order, so the waits for one stage's A leave
+    // the same stage's B in flight.
+    auto load_a = [&](int ss) {
+#pragma unroll
+      for (int i = 0; i < RA; ++i)
+        ra[i] = ld16(abase_g + static_cast<int64_t>(asrc[i]) * p.a_pitch +
+                     static_cast<int64_t>(ss) * SS);
+      if constexpr (C::FP8) as_reg = asc[ss * KB];
+    };
+    auto load_b = [&](u32x8 (&dst)[NMAT][NPR], float (&sdst)[NMAT][C::FP8 ? KB : 1], int ss) {
+      if constexpr (C::FP8) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sdst[m][kb] = bsc[m][ss * KB + kb];
+      }
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int c = 0; c < C::NPR; ++c) {
-          if (c < vp) {
-            const uint8_t *src = bptr[m] + static_cast<int64_t>(ss) * SS + c * 128;
-            dst[m][c].lo = ld16(src);
-            dst[m][c].hi = ld16(src + 64);
-          } else {
-            dst[m][c] = u32x8{0, 0, 0, 0, 0, 0, 0, 0};
-          }
+        for (int c = 0; c < NPR; ++c) {
+          const uint8_t *src = bptr[m] + static_cast<int64_t>(ss) * SS + c * 128;
+          dst[m][c].lo = ld16(src);
+          dst[m][c].hi = ld16(src + 64);
         }
-    };
-    auto load_a = [&](int ss) {
-      const int vcols = valid_pairs(ss) * 8;  // valid 16-byte columns
-#pragma unroll
-      for (int i = 0; i < RA; ++i) {
-        const int c = tid + THREADS * i;
-        if (c < ACH) {
-          const int row = c / (SS / 16), col = c % (SS / 16);
-          const int src = rowsrc[row];
-          if (src >= 0 && col < vcols)
-            ra[i] = ld16(p.A + src * p.a_pitch + static_cast<int64_t>(ss) * SS + col * 16);
-          else
-            ra[i] = u32x4{0, 0, 0, 0};
-        }
-      }
-      if constexpr (C::FP8) {
-        if (tid < BM * KB) {
-          const int src = rowsrc[tid / KB];
-          as_reg = (src >= 0 && tid % KB < valid_pairs(ss))
-                       ? p.a_scale[static_cast<int64_t>(src) * p.a_scale_pitch + ss * KB + tid % KB]
-                       : 0.0f;
-        }
-      }
     };
     auto store_a = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < RA; ++i) {
-        const int c = tid + THREADS * i;
-        if (c < ACH) {
-          const int row = c / (SS / 16), col = c % (SS / 16);
-          st16(lds + buf * BM * APITCH + row * APITCH + col * 16, ra[i]);
-        }
-      }
+      for (int i = 0; i < RA; ++i)
+        st16(lds + buf * BM * APITCH + (arow0 + i * RPP) * APITCH + acol * 16, ra[i]);
       if constexpr (C::FP8)
         if (tid < BM * KB) sAs[buf][tid] = as_reg;
     };
@@ -195,39 +188,33 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[m][b] = f32x4{0, 0, 0, 0};
 
-    auto compute = [&](const u32x8 (&bb)[NMAT][C::NPR], int buf, int ss) {
+    auto compute = [&](const u32x8 (&bb)[NMAT][NPR], const float (&sb)[NMAT][C::FP8 ? KB : 1],
+                       int buf) {
       const uint8_t *abase = lds + buf * BM * APITCH + r16 * APITCH + q * 16;
-      const int vp = valid_pairs(ss);
       if constexpr (!C::FP8) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
           if (b < mb_active) {
 #pragma unroll
-            for (int c = 0; c < C::NPR; ++c) {
-              if (c < vp) {
-                const u32x4 a0 = ld16(abase + b * 16 * APITCH + c * 128);
-                const u32x4 a1 = ld16(abase + b * 16 * APITCH + c * 128 + 64);
+            for (int c = 0; c < NPR; ++c) {
+              const u32x4 a0 = ld16(abase + b * 16 * APITCH + c * 128);
+              const u32x4 a1 = ld16(abase + b * 16 * APITCH + c * 128 + 64);
 #pragma unroll
-                for (int m = 0; m < NMAT; ++m) {
-                  acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a0), bitcast<bf16x8>(bb[m][c].lo), acc[m][b]);
-                  acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a1), bitcast<bf16x8>(bb[m][c].hi), acc[m][b]);
-                }
+              for (int m = 0; m < NMAT; ++m) {
+                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a0), bitcast<bf16x8>(bb[m][c].lo), acc[m][b]);
+                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a1), bitcast<bf16x8>(bb[m][c].hi), acc[m][b]);
               }
             }
           }
+          // bound the A reads the compiler hoists to one row block
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        float sb[NMAT][KB];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) sb[m][kb] = kb < vp ? bsc[m][ss * KB + kb] : 0.0f;
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
           if (b < mb_active) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-              if (kb >= vp) continue;
               u32x8 a;
               a.lo = ld16(abase + b * 16 * APITCH + kb * 128);
               a.hi = ld16(abase + b * 16 * APITCH + kb * 128 + 64);
@@ -251,30 +238,36 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
       }
     };
 
-    // ---- pipeline: B one super-stage ahead in registers, A double-buffered in LDS
-    load_b(bq[0], 0);
+    // ---- pipeline: B one super-stage ahead in registers, A double-buffered
+    // in LDS.  The last stage is peeled so that every prefetch in the loop is
+    // unconditional: a load behind a branch would make the wait before the
+    // next MFMA cover the loads just issued.
     load_a(0);
+    load_b(bq[0], sbq[0], 0);
     store_a(0);
     __syncthreads();
-    auto step = [&](auto par, int ss) {
-      constexpr int P = decltype(par)::value;
-      // activation rows first: the LDS store at the end of this step waits
-      // for them, and vector loads complete in issue order, so the weight
-      // loads issued after them stay in flight across the barrier
-      if (ss + 1 < nss) {
-        load_a(ss + 1);
-        load_b(bq[P ^ 1], ss + 1);
-      }
-      compute(bq[P], ss & 1, ss);
-      if (ss + 1 < nss) store_a((ss + 1) & 1);
+    auto step = [&](auto par, int ss) {  // ss + 1 < nss
+      constexpr int P = decltype(par)::value;  // == ss & 1
+      load_a(ss + 1);
+      load_b(bq[P ^ 1], sbq[P ^ 1], ss + 1);
+      compute(bq[P], sbq[P], P);
+      store_a(P ^ 1);
       __syncthreads();
     };
-    for (int ss = 0; ss < nss; ss += 2) {
+    int ss = 0;
+    for (; ss + 2 < nss; ss += 2) {
       step(std::integral_constant<int, 0>{}, ss);
-      if (ss + 1 < nss) step(std::integral_constant<int, 1>{}, ss + 1);
+      step(std::integral_constant<int, 1>{}, ss + 1);
     }
+    if (ss + 1 < nss) {
+      step(std::integral_constant<int, 0>{}, ss);
+      compute(bq[1], sbq[1], 1);
+    } else {
+      compute(bq[0], sbq[0], 0);
+    }
+    __syncthreads();
 
-    // ---- epilogue (A buffers are free: every wave passed the last barrier)
+    // ---- epilogue (A buffers are free: every wave passed the barrier above)
     if constexpr (SWIGLU && C::FP8) {
       // W8A8: z = silu(g) * u stays fp32 here; the 1x128 quantiser runs on
       // it afterwards (a quantisation group spans two items of 64 columns)
@@ -288,7 +281,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
         }
       __syncthreads();
       constexpr int PIECES = BM * BN * 4 / 16;
-      for (int c = tid; c < PIECES; c += THREADS) {
+      for (int c = tid; c < PIECES; c += C::kThreads) {
         const int row = c / (BN * 4 / 16), col = c % (BN * 4 / 16);
         if (row < rows)
           st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 4 + col * 16,
@@ -306,7 +299,7 @@ __global__ __launch_bounds__(WAVES * 64) void stream_gemm_kernel(const GemmArgs 
         }
       __syncthreads();
       constexpr int PIECES = BM * BN * 2 / 16;
-      for (int c = tid; c < PIECES; c += THREADS) {
+      for (int c = tid; c < PIECES; c += C::kThreads) {
         const int row = c / (BN * 2 / 16), col = c % (BN * 2 / 16);
         if (row < rows)
           st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
@@ -345,20 +338,33 @@ hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
 hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
                               hipStream_t s) {
   const bool gu = kind == GemmKind::GateUp;
+  const int64_t es = elem == 2 ? 1 : 2;
+  // every group's K (bytes per row) must be whole super-stages
+  auto fits = [&](int64_t ss) { return (a.K * es) % ss == 0 && (a.Ks * es) % ss == 0; };
   if (elem == 1) {
-    if (bm == 64)
-      return gu ? launch_stream<Elem::BF16, 4, 64, 512, true>(a, s)
-                : launch_stream<Elem::BF16, 8, 64, 128, false>(a, s);
-    if (bm == 128)
-      return gu ? launch_stream<Elem::BF16, 4, 128, 256, true>(a, s)
-                : launch_stream<Elem::BF16, 8, 128, 256, false>(a, s);
+    if (bm == 64) {
+      if (gu)
+        return fits(512) ? launch_stream<Elem::BF16, 4, 64, 512, true>(a, s)
+                         : launch_stream<Elem::BF16, 4, 64, 128, true>(a, s);
+      return launch_stream<Elem::BF16, 8, 64, 256, false>(a, s);
+    }
+    if (bm == 128) {
+      if (gu)
+        return fits(256) ? launch_stream<Elem::BF16, 4, 128, 256, true>(a, s)
+                         : launch_stream<Elem::BF16, 4, 128, 128, true>(a, s);
+      return fits(256) ? launch_stream<Elem::BF16, 8, 128, 256, false>(a, s)
+                       : launch_stream<Elem::BF16, 8, 128, 128, false>(a, s);
+    }
   } else if (elem == 2) {
-    if (bm == 64)
-      return gu ? launch_stream<Elem::FP8, 4, 64, 512, true>(a, s)
-                : launch_stream<Elem::FP8, 4, 64, 512, false>(a, s);
+    if (bm == 64) {
+      if (gu)
+        return fits(512) ? launch_stream<Elem::FP8, 4, 64, 512, true>(a, s)
+                         : launch_stream<Elem::FP8, 4, 64, 128, true>(a, s);
+      return launch_stream<Elem::FP8, 4, 64, 128, false>(a, s);
+    }
     if (bm == 128)
-      return gu ? launch_stream<Elem::FP8, 4, 128, 256, true>(a, s)
-                : launch_stream<Elem::FP8, 4, 128, 256, false>(a, s);
+      return gu ? launch_stream<Elem::FP8, 4, 128, 128, true>(a, s)
+                : launch_stream<Elem::FP8, 8, 128, 128, false>(a, s);
   }
   return hipErrorInvalidValue;
 }
