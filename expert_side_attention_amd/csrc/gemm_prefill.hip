@@ -155,23 +155,41 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    if (s + kRing - 1 < nst) issue(s + kRing - 1);
+    // both K steps' fragments first; the loads of stage s + 3 go out one
+    // at a time between the first K step's MFMAs, so a busy load queue
+    // never holds the wave before its matrix work
+    const bool do_issue = s + kRing - 1 < nst;
+    const int si = s + kRing - 1;
+    uint8_t *slot = lds + (si % kRing) * kSlot;
     const uint8_t *la = lds + (s % kRing) * kSlot;
     const uint8_t *lb = la + kBM * kStage;
+    bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int ch = 2 * ks + g;
-      bf16x8 fa[4], fb[2];
-      fb[0] = bitcast<bf16x8>(ld16(lb + swz64(wrow0, ch)));
-      fb[1] = bitcast<bf16x8>(ld16(lb + swz64(wrow1, ch)));
+      fb[ks][0] = bitcast<bf16x8>(ld16(lb + swz64(wrow0, ch)));
+      fb[ks][1] = bitcast<bf16x8>(ld16(lb + swz64(wrow1, ch)));
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        fa[m] = bitcast<bf16x8>(ld16(la + swz64(wr * 128 + m * 32 + r32, ch)));
+        fa[ks][m] = bitcast<bf16x8>(ld16(la + swz64(wr * 128 + m * 32 + r32, ch)));
+    }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+          acc[m][n] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][m], fb[ks][n], acc[m][n], 0, 0, 0);
+        if (ks == 0 && do_issue) {
+          const int hh = m >> 1;
+          if ((m & 1) == 0)
+            dma16(asrc[hh] + static_cast<int64_t>(si) * kStage, slot + (wave * 2 + hh) * 1024);
+          else
+            dma16(bsrc[hh] + static_cast<int64_t>(si) * kStage,
+                  slot + kBM * kStage + (wave * 2 + hh) * 1024);
+        }
+      }
     }
   }
   __syncthreads();  // all waves are done with the ring before the epilogue reuses it
