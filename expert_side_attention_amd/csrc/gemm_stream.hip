@@ -72,9 +72,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU>;
   constexpr int NMAT = C::NMAT, BN = C::BN, MB = C::MB, NPR = C::NPR;
   constexpr int APITCH = C::APITCH, CPR = C::CPR, RPP = C::RPP, RA = C::RA, KB = C::KB;
+  constexpr int SKB = C::FP8 ? KB : 1;
 
   __shared__ __align__(16) uint8_t lds[C::LDS];
-  __shared__ float sAs[2][C::FP8 ? BM * KB : 1];
+  // fp8: activation scale x weight block scale, [buffer][matrix][K block][row]
+  __shared__ __align__(16) float sAs[2][NMAT][C::FP8 ? KB : 1][C::FP8 ? BM : 4];
   __shared__ int s_item;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -174,12 +176,27 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
           dst[m][c].hi = ld16(src + 64);
         }
     };
-    auto store_a = [&](int buf) {
+    // sb: the B scales of the same stage (their loads were issued before
+    // the B rows, so waiting for them leaves the B rows in flight)
+    auto store_a = [&](int buf, const float (&sb)[NMAT][SKB]) {
 #pragma unroll
       for (int i = 0; i < RA; ++i)
         st16(lds + buf * BM * APITCH + (arow0 + i * RPP) * APITCH + acol * 16, ra[i]);
       if constexpr (C::FP8)
-        if (tid < BM * KB) sAs[buf][tid] = as_reg;
+        if (tid < BM * KB) {
+          const int kb = tid % KB;
+          float sbk[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            // select the block without dynamic register indexing
+            float v = sb[m][0];
+#pragma unroll
+            for (int k2 = 1; k2 < SKB; ++k2) v = kb == k2 ? sb[m][k2] : v;
+            sbk[m] = v;
+          }
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) sAs[buf][m][kb][tid / KB] = as_reg * sbk[m];
+        }
     };
 
     f32x4 acc[NMAT][MB];
@@ -218,17 +235,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
               u32x8 a;
               a.lo = ld16(abase + b * 16 * APITCH + kb * 128);
               a.hi = ld16(abase + b * 16 * APITCH + kb * 128 + 64);
-              float sa[4];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sa[i] = sAs[buf][(b * 16 + q * 4 + i) * KB + kb];
 #pragma unroll
               for (int m = 0; m < NMAT; ++m) {
+                const f32x4 sab = *reinterpret_cast<const f32x4 *>(&sAs[buf][m][kb][b * 16 + q * 4]);
                 const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, bb[m][kb]),
                     f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  acc[m][b][i] = fmaf(part[i], sa[i] * sb[m][kb], acc[m][b][i]);
+                for (int i = 0; i < 4; ++i) acc[m][b][i] = fmaf(part[i], sab[i], acc[m][b][i]);
               }
             }
           }
@@ -244,14 +258,14 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     // next MFMA cover the loads just issued.
     load_a(0);
     load_b(bq[0], sbq[0], 0);
-    store_a(0);
+    store_a(0, sbq[0]);
     __syncthreads();
     auto step = [&](auto par, int ss) {  // ss + 1 < nss
       constexpr int P = decltype(par)::value;  // == ss & 1
       load_a(ss + 1);
       load_b(bq[P ^ 1], sbq[P ^ 1], ss + 1);
       compute(bq[P], sbq[P], P);
-      store_a(P ^ 1);
+      store_a(P ^ 1, sbq[P ^ 1]);
       __syncthreads();
     };
     int ss = 0;
@@ -358,12 +372,13 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
   } else if (elem == 2) {
     if (bm == 64) {
       if (gu)
-        return fits(512) ? launch_stream<Elem::FP8, 4, 64, 512, true>(a, s)
+        return fits(256) ? launch_stream<Elem::FP8, 4, 64, 256, true>(a, s)
                          : launch_stream<Elem::FP8, 4, 64, 128, true>(a, s);
       return launch_stream<Elem::FP8, 4, 64, 128, false>(a, s);
     }
     if (bm == 128)
-      return gu ? launch_stream<Elem::FP8, 4, 128, 128, true>(a, s)
+      return gu ? (fits(256) ? launch_stream<Elem::FP8, 4, 128, 256, true>(a, s)
+                          : launch_stream<Elem::FP8, 4, 128, 128, true>(a, s))
                 : launch_stream<Elem::FP8, 8, 128, 128, false>(a, s);
   }
   return hipErrorInvalidValue;
