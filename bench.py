@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward captured in a HIP graph and replayed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (profiler calibration)")
     args = ap.parse_args()
@@ -247,6 +249,32 @@ def main():
     torch.cuda.synchronize()
     ms_serial = (time.perf_counter() - ts0) * 1e3 / max(1, args.steps // 4)
 
+    graph_ms = None
+    if args.graph:
+        # one step captured in a HIP graph (all micro-batches, each on its
+        # own stream, forked from and joined into the capture stream)
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            if nmb == 1:
+                layers[0].forward(xs[0], out=outs[0], stream=cap)
+            else:
+                fork = torch.cuda.Event()
+                fork.record(cap)
+                for li, xi, oi, st in zip(layers, xs, outs, streams):
+                    st.wait_event(fork)
+                    li.forward(xi, out=oi, stream=st)
+                    cap.wait_stream(st)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg0) * 1e3 / args.steps
+
     ai = model["forward_flops"] / model["forward_bytes"]
     ridge = MFMA_PEAK_TFLOPS[shape.mode] * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "mfma" if ai > ridge else "hbm"
@@ -299,6 +327,7 @@ def main():
                                        / MFMA_PEAK_TFLOPS[shape.mode], 4),
                     "touched_experts": model["touched_experts"],
                     "micro_batches": nmb, "ms_serial_one_stream": round(ms_serial, 5),
+                    "ms_graph_replay": None if graph_ms is None else round(graph_ms, 5),
                     "stage_ms": stages},
         "cpu_baseline": None,
         "kernel_source_hash": res_hash,

@@ -1,0 +1,63 @@
+"""A forward captured in a HIP graph and replayed equals the eager forward.
+
+The FFN service of the AFD plugin runs decode as a captured graph (vLLM AFD
+Plugin page, connector table: the synchronous connectors use full-decode
+graph mode), so `afd_ffn_forward` must be capturable: it enqueues kernels
+only, never allocates, synchronises or reads device memory on the host.
+
+Every replay is checked bitwise against the eager result for the same input,
+with eager forwards and synchronisations of the program in between, over
+several replays and inputs that route differently.
+"""
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from afd_inputs import LayerShape, SyntheticLayer  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(shape, seed):
+    from expert_side_attention_amd.workload import build_layer, hidden_tensor
+    syn = SyntheticLayer(shape, seed=seed)
+    return build_layer(syn, "cuda:0"), hidden_tensor(syn, "cuda:0")
+
+
+@pytest.mark.parametrize("shape", [
+    LayerShape("graph_bf16", T=128, h=256, E=16, k=4, I=256, S=1, Is=256, mode="bf16"),
+    LayerShape("graph_w8a8", T=96, h=256, E=8, k=2, I=256, S=1, Is=128, mode="w8a8"),
+    LayerShape("graph_prefill", T=1200, h=256, E=4, k=2, I=256, S=1, Is=128, mode="bf16"),
+], ids=lambda s: s.name)
+def test_graph_replay_matches_eager(shape):
+    layer, x = _layer(shape, seed=11)
+    # three inputs with different routing: the batch, its rows rolled, and
+    # rows negated (exact in bf16; flips the sign of every logit)
+    inputs = [x, torch.roll(x, shifts=37, dims=0).contiguous(), (-x).contiguous()]
+    eager = [layer.forward(xi).clone() for xi in inputs]
+    torch.cuda.synchronize()
+
+    s = torch.cuda.Stream()
+    x_static = torch.empty_like(x)
+    out_static = torch.empty_like(x)
+    with torch.cuda.stream(s):
+        x_static.copy_(inputs[0])
+        layer.forward(x_static, out=out_static, stream=s)  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        layer.forward(x_static, out=out_static, stream=s)
+    torch.cuda.synchronize()
+
+    scratch = torch.empty_like(x)
+    for rep in range(3):
+        for i, xi in enumerate(inputs):
+            x_static.copy_(xi)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out_static, eager[i]), f"replay {rep} input {i}"
+            # eager work of the program between replays
+            layer.forward(inputs[(i + 1) % 3], out=scratch)
+            torch.cuda.synchronize()
+            assert torch.equal(scratch, eager[(i + 1) % 3])
+    layer.close()
