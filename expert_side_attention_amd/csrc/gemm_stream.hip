@@ -377,7 +377,7 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
       return launch_stream<Elem::FP8, 4, 64, 128, false>(a, s);
     }
     if (bm == 128)
-      return gu ? (fits(256) ? launch_stream<Elem::FP8, 4, 128, 256, true>(a, s)
+      return gu ? (fits(256) ? launch_stream<Elem::FP8, 8, 128, 256, true>(a, s)
                           : launch_stream<Elem::FP8, 4, 128, 128, true>(a, s))
                 : launch_stream<Elem::FP8, 8, 128, 128, false>(a, s);
   }
