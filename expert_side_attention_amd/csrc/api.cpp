@@ -360,9 +360,11 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   g.c_pitch = static_cast<int64_t>(h->zpitch) * zes;
   g.c_scale = h->zs;
   g.c_scale_pitch = h->zpitch / 128;
-  // W8A8 on the streaming kernels: gate/up writes fp32 z, then the 1x128
-  // quantiser produces the E4M3 rows and scales the down GEMM reads
-  const bool z_fp32 = h->elem == 2 && plan.small_kernel == afd::GemmKernel::Stream;
+  // W8A8 on the streaming kernels with 64-row tiles: gate/up writes fp32 z,
+  // then the 1x128 quantiser produces the E4M3 rows and scales the down GEMM
+  // reads (with 128-row tiles the gate/up epilogue quantises itself)
+  const bool z_fp32 = h->elem == 2 && plan.small_kernel == afd::GemmKernel::Stream &&
+                      !afd::stream_gate_up_writes_fp8(h->elem, plan.tiles.bm_small);
   if (z_fp32) {
     g.C = reinterpret_cast<uint8_t *>(h->z32);
     g.c_pitch = static_cast<int64_t>(h->zpitch) * 4;

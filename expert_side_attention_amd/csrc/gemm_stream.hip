@@ -283,8 +283,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 
     // ---- epilogue (A buffers are free: every wave passed the barrier above)
     if constexpr (SWIGLU && C::FP8) {
-      // W8A8: z = silu(g) * u stays fp32 here; the 1x128 quantiser runs on
-      // it afterwards (a quantisation group spans two items of 64 columns)
+      // W8A8: z = silu(g) * u in fp32, staged in LDS
       float *o32 = reinterpret_cast<float *>(lds);
 #pragma unroll
       for (int b = 0; b < MB; ++b)
@@ -294,12 +293,58 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
           o32[row * BN + wave * 16 + r16] = silu_mul(acc[0][b][i], acc[1][b][i]);
         }
       __syncthreads();
-      constexpr int PIECES = BM * BN * 4 / 16;
-      for (int c = tid; c < PIECES; c += C::kThreads) {
-        const int row = c / (BN * 4 / 16), col = c % (BN * 4 / 16);
-        if (row < rows)
-          st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 4 + col * 16,
-               ld16(lds + row * BN * 4 + col * 16));
+      if constexpr (BN == 128) {
+        // the item is exactly one 1x128 quantisation group wide: four
+        // threads per row take 32 columns each, share the row's amax and
+        // write E4M3 codes and the group scale (same arithmetic as the
+        // standalone quantiser)
+        constexpr int TPR = C::kThreads / BM;  // threads per row
+        static_assert(TPR * 32 == BN && TPR <= 64 && (64 % TPR) == 0, "row split");
+        for (int row = tid / TPR; row < BM; row += C::kThreads / TPR) {
+          const int part = tid % TPR;
+          const float *src = o32 + row * BN + part * 32;
+          float f[32];
+#pragma unroll
+          for (int c4 = 0; c4 < 8; ++c4) {
+            const u32x4 v = ld16(src + c4 * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[c4 * 4 + i] = __uint_as_float(v[i]);
+          }
+          float amax = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+          for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+          const float sc = e4m3_scale(amax);
+          if (row < rows) {
+            uint8_t *dst = p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 + part * 32;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              uint32_t w[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+                  word |= f32_to_e4m3(f[h2 * 16 + j * 4 + bb] / sc) << (8 * bb);
+                w[j] = word;
+              }
+              st16(dst + h2 * 16, u32x4{w[0], w[1], w[2], w[3]});
+            }
+            if (part == 0)
+              p.c_scale[static_cast<int64_t>(tile.row0 + row) * p.c_scale_pitch + n0 / 128] = sc;
+          }
+        }
+      } else {
+        // a quantisation group spans two items: z stays fp32 and the 1x128
+        // quantiser runs on it afterwards
+        constexpr int PIECES = BM * BN * 4 / 16;
+        for (int c = tid; c < PIECES; c += C::kThreads) {
+          const int row = c / (BN * 4 / 16), col = c % (BN * 4 / 16);
+          if (row < rows)
+            st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 4 + col * 16,
+                 ld16(lds + row * BN * 4 + col * 16));
+        }
       }
     } else {
       uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
@@ -349,6 +394,8 @@ hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
+bool stream_gate_up_writes_fp8(int elem, int bm) { return elem == 2 && bm == 128; }
+
 hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
                               hipStream_t s) {
   const bool gu = kind == GemmKind::GateUp;
@@ -377,8 +424,9 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
       return launch_stream<Elem::FP8, 4, 64, 128, false>(a, s);
     }
     if (bm == 128)
+      // both gate/up shapes are 128 columns wide: stream_gate_up_writes_fp8
       return gu ? (fits(256) ? launch_stream<Elem::FP8, 8, 128, 256, true>(a, s)
-                          : launch_stream<Elem::FP8, 4, 128, 128, true>(a, s))
+                          : launch_stream<Elem::FP8, 8, 128, 128, true>(a, s))
                 : launch_stream<Elem::FP8, 8, 128, 128, false>(a, s);
   }
   return hipErrorInvalidValue;

@@ -98,7 +98,10 @@ GemmPlan gemm_plan(int elem, int T, int k, int E);
 // LDS-tiled kernel (all element types).
 hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,
                        hipStream_t s);
-// Weight-streaming persistent kernel (bf16, fp8; bm 64 or 128).
+// Weight-streaming persistent kernel (bf16, fp8; bm 64 or 128).  W8A8
+// gate/up writes E4M3 z and 1x128 scales itself when this returns true,
+// else fp32 z for the standalone quantiser.
+bool stream_gate_up_writes_fp8(int elem, int bm);
 hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
                               hipStream_t s);
 // Compute-bound kernel (bf16, bm 256).

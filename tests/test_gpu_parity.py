@@ -76,6 +76,7 @@ SMALL = [
     LayerShape("w8a8_small", T=200, h=512, E=8, k=2, I=256, S=1, Is=384, mode="w8a8"),
     LayerShape("w8a8_many", T=96, h=256, E=32, k=8, I=384, mode="w8a8"),
     LayerShape("w8a8_dense", T=600, h=256, E=8, k=2, I=256, S=1, Is=128, mode="w8a8"),
+    LayerShape("w8a8_h384", T=200, h=384, E=8, k=2, I=256, S=1, Is=384, mode="w8a8"),
     LayerShape("bf16_dense", T=700, h=256, E=4, k=1, I=128, S=1, Is=384, mode="bf16"),
     LayerShape("bf16_prefill_h384", T=520, h=384, E=4, k=2, I=256, S=1, Is=128, mode="bf16"),
     LayerShape("bf16_prefill_skew", T=1500, h=256, E=16, k=2, I=256, S=1, Is=256,
