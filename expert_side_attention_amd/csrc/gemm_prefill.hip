@@ -23,6 +23,8 @@
 // go to XCDs round-robin) and all column tiles of a row tile run on one XCD,
 // close in time: the XCD's L2 serves the activation rows to all of them.
 #include "common.h"
+#include <atomic>
+
 #include "kernels.h"
 
 namespace afd {
@@ -227,12 +229,18 @@ template <bool SWIGLU>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
   constexpr size_t kLds = kRing * kSlot;  // 128 KB
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_gemm_kernel<SWIGLU>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  // the dynamic-LDS limit is a per-device attribute of the kernel
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> attr_set[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_gemm_kernel<SWIGLU>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev].store(true, std::memory_order_release);
   }
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int ntn = (nmax + BNO - 1) / BNO;

@@ -26,6 +26,7 @@
 //  * Epilogues stage the tile through LDS and write whole 16-byte pieces;
 //    the fp8 gate/up epilogue writes z in fp32 for the 1x128 quantiser.
 #include "common.h"
+#include <atomic>
 #include <type_traits>
 
 #include "kernels.h"
@@ -372,20 +373,29 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
 hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
   auto kern = stream_gemm_kernel<EL, WAVES, BM, SS, SWIGLU>;
-  static int per_cu = -1, cus = 0;
-  if (per_cu < 0) {
-    int dev = 0;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void *>(kern), WAVES * 64, 0);
+  // resident workgroups of this kernel on the current device (cached per device)
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> resident[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int slots = resident[dev].load(std::memory_order_relaxed);
+  if (slots <= 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(kern),
+                                                     WAVES * 64, 0);
     if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    slots = cus * per_cu;
+    resident[dev].store(slots, std::memory_order_relaxed);
   }
   constexpr int BN = 16 * WAVES;
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int64_t items = static_cast<int64_t>(a.tiles_ub) * (nmax / BN);
   // persistent: one resident wave of workgroups
-  int64_t grid = static_cast<int64_t>(cus) * per_cu;
+  int64_t grid = slots;
   if (items < grid) grid = items;
   if (grid <= 0) return hipSuccess;
   kern<<<static_cast<unsigned>(grid), WAVES * 64, 0, s>>>(a);
