@@ -158,6 +158,31 @@ def test_determinism_and_microbatch_split():
     assert torch.equal(torch.cat([p1, p2]).view(torch.int16), a.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", [
+    # decode-regime plans: every expert's rows sit in one tile of one kernel,
+    # whose per-row arithmetic does not depend on the row's position
+    LayerShape("perm_bf16_bm128", T=300, h=256, E=16, k=4, I=256, S=1, Is=128, mode="bf16"),
+    LayerShape("perm_bf16_bm64", T=100, h=256, E=32, k=4, I=256, mode="bf16"),
+    LayerShape("perm_w8a8_bm128", T=200, h=256, E=8, k=2, I=256, S=1, Is=128, mode="w8a8"),
+    LayerShape("perm_w8a8_bm64", T=96, h=256, E=32, k=8, I=128, mode="w8a8"),
+    LayerShape("perm_f32", T=64, h=128, E=8, k=2, I=128, S=1, Is=128, mode="f32"),
+], ids=lambda s: s.name)
+def test_token_permutation_equivariance(shape):
+    """Permuting the tokens permutes the output rows, bit for bit: routing,
+    dispatch order and tiles change, the arithmetic of each token does not."""
+    syn = SyntheticLayer(shape, seed=13)
+    from expert_side_attention_amd.workload import build_layer, to_device
+    layer = build_layer(syn, DEV)
+    x = to_device(syn.hidden(), DEV, shape.mode != "f32")
+    perm = torch.randperm(shape.T, generator=torch.Generator().manual_seed(5)).to(DEV)
+    a = layer.forward(x).clone()
+    b = layer.forward(x[perm].contiguous()).clone()
+    torch.cuda.synchronize()
+    iv = torch.int32 if shape.mode == "f32" else torch.int16
+    assert torch.equal(b.view(iv), a[perm].view(iv))
+    layer.close()
+
+
 def test_two_streams_two_handles_match_serial():
     shape = LayerShape("streams", T=512, h=256, E=16, k=4, I=256, S=1, Is=256, mode="bf16")
     syn = SyntheticLayer(shape, seed=7)
