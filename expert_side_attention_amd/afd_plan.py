@@ -1,0 +1,75 @@
+"""Attention:FFN pool planning from measured stage times (host side, not on
+the kernel path).
+
+Rules restated from the pages:
+* Rate matching: the fraction of the GPUs given to attention follows
+  attention's fraction of the per-step cost, with at least one attention GPU
+  and the rest for the experts (AFD Disagg MoE notes page, case 2 on
+  capacity alignment).  The nearest integer is taken with ties to even, the
+  rounding of the language the page's example is written in.
+* Micro-pipeline: with attention and FFN on separate pools the steady period
+  is the longer stage plus the hand-over, max(t_a, t_f) + t_comm, against
+  t_a + t_f when both run on the same GPUs (A/F 分离 page, 深入推导, 微流水).
+* Rank layout: FFN ranks come first; the attention rank count must be at
+  least the FFN rank count and a whole multiple of it (vLLM AFD plugin page
+  in Spanish, "Con qué te vas a tropezar": 64A16F is legal, 16A64F and 64A24F
+  are not).
+* Traffic: dispatch plus combine move factor * h * k * bytes_per_elem * 2
+  bytes per token per layer, factor = 2 as the A/F page prints it (深入推导,
+  通信账).
+"""
+from __future__ import annotations
+
+import json
+
+
+def split_gpus(attn_cost: float, ffn_cost: float, total_gpus: int):
+    """(attention GPUs, FFN GPUs) for stage costs measured in the same unit."""
+    if total_gpus < 2:
+        raise ValueError("need at least one GPU per pool")
+    if attn_cost < 0 or ffn_cost < 0 or attn_cost + ffn_cost <= 0:
+        raise ValueError("costs must be non-negative and not both zero")
+    share = attn_cost / (attn_cost + ffn_cost)
+    n_attn = round(total_gpus * share)  # nearest, ties to even
+    n_attn = min(max(n_attn, 1), total_gpus - 1)
+    return n_attn, total_gpus - n_attn
+
+
+def check_rank_counts(num_attention_ranks: int, num_ffn_ranks: int) -> None:
+    """Raise ValueError unless the plugin's rank rule holds."""
+    a, f = num_attention_ranks, num_ffn_ranks
+    if f < 1 or a < 1:
+        raise ValueError("each role needs at least one rank")
+    if a < f:
+        raise ValueError(f"{a}A{f}F: attention ranks must not be fewer than FFN ranks")
+    if a % f:
+        raise ValueError(f"{a}A{f}F: attention ranks must be a multiple of FFN ranks")
+
+
+def rank_roles(num_attention_ranks: int, num_ffn_ranks: int):
+    """Role of each global rank: FFN ranks first, then attention ranks."""
+    check_rank_counts(num_attention_ranks, num_ffn_ranks)
+    return ["ffn"] * num_ffn_ranks + ["attention"] * num_attention_ranks
+
+
+def pipeline_period(t_a: float, t_f: float, t_comm: float = 0.0):
+    """Steady per-step period co-located vs disaggregated, same time unit."""
+    colocated = t_a + t_f
+    disaggregated = max(t_a, t_f) + t_comm
+    return {"colocated": colocated, "disaggregated": disaggregated,
+            "gain": colocated / disaggregated if disaggregated > 0 else float("inf")}
+
+
+def comm_bytes_per_token_layer(h: int, k: int, bytes_per_elem: int = 1, factor: int = 2) -> int:
+    """Dispatch + combine bytes per token per layer as the A/F page counts them."""
+    return factor * h * k * bytes_per_elem * 2
+
+
+def ffn_step_ms(bench_json_path: str) -> float:
+    """Measured FFN layer time per step (ms) from a bench.py JSON line file."""
+    with open(bench_json_path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                return float(json.loads(line)["ms_per_step"])
+    raise ValueError(f"no bench line in {bench_json_path}")
