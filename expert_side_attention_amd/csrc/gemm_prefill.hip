@@ -6,18 +6,21 @@
 //
 // Tile: 256 rows x 256 weight rows per workgroup (gate/up: 128 gate + 128 up
 // rows, i.e. 128 output columns of z; down: 256 output columns), K in
-// 32-element (64-byte) stages.  Eight waves (two per SIMD) in a 2 x 4 grid
-// each own 128 rows x 64 weight rows = 4 x 2 tiles of 32x32x16 MFMAs (128
-// fp32 accumulators per lane); for gate/up a wave's two column blocks are a
-// gate block and the up block of the same columns.
+// 64-element (128-byte) stages, so every load request is a whole cache line.
+// Eight waves (two per SIMD) in a 2 x 4 grid each own 128 rows x 64 weight
+// rows = 4 x 2 tiles of 32x32x16 MFMAs (128 fp32 accumulators per lane); for
+// gate/up a wave's two column blocks are a gate block and the up block of
+// the same columns.
 //
 // Operands move with direct-to-LDS loads (global_load_lds, no staging
-// registers) into a ring of 4 stage slots, so three stages (96 KB) are in
-// flight per workgroup while the MFMAs read the fourth: with one stage in
-// flight the loads could not keep up with the MFMAs.  Ordering uses
-// explicit vmcnt waits plus a bare s_barrier per stage (a full workgroup
-// fence would drain every outstanding load).  LDS rows are 64 bytes with the
-// 16-byte chunk index XOR-ed by (row / 4) % 4 against bank conflicts.
+// registers) into two 64 KB stage buffers: the next stage loads while the
+// MFMAs read the current one, its loads issued one at a time between the
+// first K steps' MFMAs.  Ordering uses an explicit vmcnt wait plus a bare
+// s_barrier per stage (a full workgroup fence would drain every outstanding
+// load).  LDS rows are 128 bytes with the 16-byte chunk index XOR-ed by
+// (row / 2) % 8, so the 16 rows one MFMA operand read touches per quarter
+// wave hit 16 different 4-bank groups.  (32-element stages in a deeper ring
+// fetched half lines and ran 7-9% slower.)
 //
 // Tile order: row tiles are dealt round-robin to the 8 XCDs (workgroup ids
 // go to XCDs round-robin) and all column tiles of a row tile run on one XCD,
@@ -34,15 +37,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;    // rows per tile
 constexpr int kBW = 256;    // weight rows per tile
-constexpr int kStage = 64;  // bytes per row per K stage (32 bf16)
-constexpr int kRing = 4;    // LDS ring of stages (3 in flight)
-constexpr int kSlot = (kBM + kBW) * kStage;  // 32 KB
+constexpr int kStage = 128;  // bytes per row per K stage (64 bf16)
+constexpr int kRing = 2;    // LDS double buffer
+constexpr int kSlot = (kBM + kBW) * kStage;  // 64 KB
 
-// byte offset of 16-byte chunk `chunk` (0..3) of LDS row `row`: the chunk
-// index is XOR-ed with (row / 4) % 4 so that the 16 rows one MFMA operand
-// read touches per half-wave hit 16 different 4-bank groups
+// byte offset of 16-byte chunk `chunk` (0..7) of LDS row `row`: the chunk
+// index is XOR-ed with (row / 2) % 8 (see the file comment)
 __device__ __forceinline__ int swz64(int row, int chunk) {
-  return row * kStage + ((chunk ^ ((row >> 2) & 3)) << 4);
+  return row * kStage + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -59,7 +61,7 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_dst) {
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
-  extern __shared__ __align__(16) uint8_t lds[];  // kRing x (A 16 KB + B 16 KB)
+  extern __shared__ __align__(16) uint8_t lds[];  // kRing x (A 32 KB + B 32 KB)
   __shared__ int rowsrc[kBM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -100,19 +102,19 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   const uint8_t *B1 = SWIGLU ? (shared ? p.sb1 : p.b1) + gi * mat : B0;
 
   // Each wave moves rows [32 wave, 32 wave + 32) of the A stage and of the
-  // B stage: two 1 KB direct-to-LDS loads each (16 rows of 64 bytes per
-  // load).  Lane i fills LDS row 16 h + i / 4, position i % 4, which holds
-  // the row's 16-byte chunk (i % 4) ^ ((row / 4) % 4) (bank swizzle).
+  // B stage: four 1 KB direct-to-LDS loads each (8 rows of 128 bytes per
+  // load).  Lane i fills LDS row 8 h + i / 8, position i % 8, which holds
+  // the row's 16-byte chunk (i % 8) ^ ((row / 2) % 8) (bank swizzle).
   // Rows past the tile's end load a valid row (rows of an MFMA tile are
   // independent; those results are never stored); weight rows past N (a
   // partial last column tile) load row N - 1.
   const int src_first = rowsrc[0];
-  const uint8_t *asrc[2];
-  const uint8_t *bsrc[2];
+  const uint8_t *asrc[4];
+  const uint8_t *bsrc[4];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int row = wave * 32 + hh * 16 + (lane >> 2);
-    const int ch = (lane & 3) ^ ((row >> 2) & 3);
+  for (int hh = 0; hh < 4; ++hh) {
+    const int row = wave * 32 + hh * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);
     const int src = rowsrc[row] >= 0 ? rowsrc[row] : src_first;
     asrc[hh] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
     const int n = n0 + (SWIGLU ? (row & (kBW / 2 - 1)) : row);
@@ -122,10 +124,10 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   auto issue = [&](int s) {  // stage s -> ring slot s % kRing
     uint8_t *slot = lds + (s % kRing) * kSlot;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      dma16(asrc[hh] + static_cast<int64_t>(s) * kStage, slot + (wave * 2 + hh) * 1024);
+    for (int hh = 0; hh < 4; ++hh) {
+      dma16(asrc[hh] + static_cast<int64_t>(s) * kStage, slot + (wave * 4 + hh) * 1024);
       dma16(bsrc[hh] + static_cast<int64_t>(s) * kStage,
-            slot + kBM * kStage + (wave * 2 + hh) * 1024);
+            slot + kBM * kStage + (wave * 4 + hh) * 1024);
     }
   };
 
@@ -140,56 +142,41 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   const int wrow0 = SWIGLU ? wc * 32 + r32 : wc * 64 + r32;
   const int wrow1 = SWIGLU ? kBW / 2 + wc * 32 + r32 : wc * 64 + 32 + r32;
 
-  // prologue: stages 0 .. kRing-2 in flight
+  // prologue: stage 0 in flight
 #pragma unroll
   for (int s = 0; s < kRing - 1; ++s)
     if (s < nst) issue(s);
   for (int s = 0; s < nst; ++s) {
-    // this wave's loads of stage s are done when at most the loads of the
-    // later stages already issued (4 per stage) are outstanding; the
-    // barrier then covers every wave's loads, and also guarantees that all
-    // waves finished reading the slot the next issue overwrites
-    const int later = min(kRing - 2, nst - 1 - s);
-    if (later >= 2)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // double buffer: only stage s is in flight here
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    // both K steps' fragments first; the loads of stage s + 3 go out one
-    // at a time between the first K step's MFMAs, so a busy load queue
-    // never holds the wave before its matrix work
-    const bool do_issue = s + kRing - 1 < nst;
-    const int si = s + kRing - 1;
+    const bool do_issue = s + 1 < nst;
+    const int si = s + 1;
     uint8_t *slot = lds + (si % kRing) * kSlot;
     const uint8_t *la = lds + (s % kRing) * kSlot;
     const uint8_t *lb = la + kBM * kStage;
-    bf16x8 fa[2][4], fb[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
       const int ch = 2 * ks + g;
-      fb[ks][0] = bitcast<bf16x8>(ld16(lb + swz64(wrow0, ch)));
-      fb[ks][1] = bitcast<bf16x8>(ld16(lb + swz64(wrow1, ch)));
+      bf16x8 fa[4], fb[2];
+      fb[0] = bitcast<bf16x8>(ld16(lb + swz64(wrow0, ch)));
+      fb[1] = bitcast<bf16x8>(ld16(lb + swz64(wrow1, ch)));
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        fa[ks][m] = bitcast<bf16x8>(ld16(la + swz64(wr * 128 + m * 32 + r32, ch)));
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+        fa[m] = bitcast<bf16x8>(ld16(la + swz64(wr * 128 + m * 32 + r32, ch)));
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
-          acc[m][n] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][m], fb[ks][n], acc[m][n], 0, 0, 0);
-        if (ks == 0 && do_issue) {
-          const int hh = m >> 1;
-          if ((m & 1) == 0)
-            dma16(asrc[hh] + static_cast<int64_t>(si) * kStage, slot + (wave * 2 + hh) * 1024);
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+        if (ks < 2 && do_issue) {
+          const int idx = ks * 4 + m;  // 0..7
+          const int hh = idx >> 1;
+          if ((idx & 1) == 0)
+            dma16(asrc[hh] + static_cast<int64_t>(si) * kStage, slot + (wave * 4 + hh) * 1024);
           else
             dma16(bsrc[hh] + static_cast<int64_t>(si) * kStage,
-                  slot + kBM * kStage + (wave * 2 + hh) * 1024);
+                  slot + kBM * kStage + (wave * 4 + hh) * 1024);
         }
       }
     }
@@ -228,7 +215,7 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
 template <bool SWIGLU>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
-  constexpr size_t kLds = kRing * kSlot;  // 128 KB
+  constexpr size_t kLds = kRing * kSlot;  // 2 x 64 KB
   // the dynamic-LDS limit is a per-device attribute of the kernel
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> attr_set[kMaxDevices];
