@@ -84,6 +84,19 @@ SMALL = [
 ]
 
 
+# long batches at small width: 64 dispatch blocks, large tile lists and grids,
+# the compute-bound bf16 kernel and the fp8 tiled kernel
+LONG = [
+    LayerShape("bf16_t65536", T=65536, h=128, E=64, k=8, I=128, S=1, Is=128, mode="bf16"),
+    LayerShape("w8a8_t32768", T=32768, h=256, E=32, k=2, I=128, S=1, Is=128, mode="w8a8"),
+]
+
+
+@pytest.mark.parametrize("shape", LONG, ids=[s.name for s in LONG])
+def test_long_batch_parity(shape):
+    check_layer(SyntheticLayer(shape, seed=21), threads=16)
+
+
 @pytest.mark.parametrize("shape", SMALL, ids=[s.name for s in SMALL])
 def test_small_layer_parity(shape):
     check_layer(SyntheticLayer(shape, seed=3))
