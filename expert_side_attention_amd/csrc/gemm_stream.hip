@@ -20,11 +20,19 @@
 //  * bf16: chunk i is one 16x16x32 MFMA.  fp8: chunks 2b and 2b+1 (bytes
 //    [128 b + 16 q] and [128 b + 64 + 16 q]) lie in the same 128-wide K
 //    block b and feed one 16x16x128 MFMA; the block's partial sum is then
-//    scaled by (activation scale of the row) x (weight block scale).
-//    A and B use the same byte->K assignment, so the products are exact
-//    permutations of the K sum.
-//  * Epilogues stage the tile through LDS and write whole 16-byte pieces;
-//    the fp8 gate/up epilogue writes z in fp32 for the 1x128 quantiser.
+//    scaled by (activation scale of the row) x (weight block scale), a
+//    product staged once per row and block in LDS.  A and B use the same
+//    byte->K assignment, so the products are exact permutations of the K
+//    sum.
+//  * Every load of the main loop is unconditional and issued A rows, A
+//    scale, B scales, B rows (the last stage is peeled): vector loads
+//    complete in order, so the wait before the A store leaves the next
+//    stage's weights in flight, and no branch makes the compiler's wait
+//    before an MFMA cover loads just issued.
+//  * Epilogues stage the tile through LDS and write whole 16-byte pieces.
+//    The fp8 gate/up epilogue of a 128-column item (one 1x128 quantisation
+//    group) writes E4M3 z and its scales; a 64-column item writes fp32 z
+//    for the standalone quantiser.
 #include "common.h"
 #include <atomic>
 #include <type_traits>
