@@ -151,6 +151,44 @@ def cpu_baseline(syn, min_seconds=10.0):
                       f"host has {cores} cores"}
 
 
+def pipeline(args):
+    """Attention/FFN ping-pong of two decode micro-batches on one GPU, in the
+    co-located, overlapped and CU-split placements."""
+    import torch
+    from afd_inputs import CONFIGS, SyntheticLayer
+    from expert_side_attention_amd import afd_pipeline as AP
+    from expert_side_attention_amd.workload import build_layer, hidden_tensor
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    shape = CONFIGS[args.workload]
+    if shape.micro_batches != 1 or shape.mode == "f32":
+        raise SystemExit("--pipeline takes a bf16 or W8A8 decode workload")
+    dev = "cuda:0"
+    M = 2
+    syn = SyntheticLayer(shape.with_tokens(M * shape.T), seed=args.seed)
+    log(f"[bench] pipeline: building {shape.name} x {M} micro-batches on {dev}")
+    ffn0 = build_layer(syn, dev, max_tokens=shape.T)
+    ffns = [ffn0, ffn0.sibling()]
+    x = hidden_tensor(syn, dev)
+    xs = [x[m * shape.T:(m + 1) * shape.T].contiguous() for m in range(M)]
+    attn = [AP.AttentionStub(shape.T, shape.h, args.pipeline_context, device=dev, seed=m + 1)
+            for m in range(M)]
+    res = AP.measure(ffns, xs, attn, layers=args.pipeline_layers, reps=max(5, args.steps // 5))
+    res.pop("finals")
+    def rounded(v):
+        if isinstance(v, dict):
+            return {k: rounded(w) for k, w in v.items()}
+        return round(v, 5) if isinstance(v, float) else v
+
+    out = {"pipeline": rounded(res),
+           "config": {"workload": shape.name, "micro_batch_tokens": shape.T, "micro_batches": M,
+                      "attention_stub": {"context": args.pipeline_context, "heads": 16, "d": 512,
+                                         "kv_bytes_per_micro_batch": attn[0].kv_bytes()}},
+           "data": "synthetic"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,9 +201,21 @@ def main():
                     help="also time the forward captured in a HIP graph and replayed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (profiler calibration)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="only run the attention/FFN micro-pipeline (two micro-batches of a "
+                         "decode workload and an attention stand-in) and print its line")
+    ap.add_argument("--pipeline-context", type=int, default=4096, metavar="L",
+                    help="KV positions per token of the attention stand-in")
+    ap.add_argument("--pipeline-layers", type=int, default=20)
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.pipeline:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only.", file=sys.stderr)
+            sys.exit(2)
+        pipeline(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the layer runs on a single MI355X "

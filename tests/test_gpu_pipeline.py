@@ -1,0 +1,42 @@
+"""The attention/FFN micro-pipeline harness: every placement of the
+ping-pong schedule (co-located on one stream, overlapped on two streams,
+split over CU-masked streams) yields the hidden states of the plain loop
+over layers and micro-batches, bit for bit."""
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from afd_inputs import LayerShape, SyntheticLayer  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def test_pipeline_placements_agree():
+    from expert_side_attention_amd import afd_pipeline as AP
+    from expert_side_attention_amd.workload import build_layer, hidden_tensor
+    T, M, layers = 64, 2, 4
+    shape = LayerShape("pipe_bf16", T=M * T, h=512, E=16, k=4, I=256, S=1, Is=256,
+                       mode="bf16")
+    syn = SyntheticLayer(shape, seed=5)
+    f0 = build_layer(syn, "cuda:0", max_tokens=T)
+    ffns = [f0, f0.sibling()]
+    x = hidden_tensor(syn, "cuda:0")
+    xs = [x[m * T:(m + 1) * T].contiguous() for m in range(M)]
+    attn = [AP.AttentionStub(T, shape.h, 256, heads=4, d=128, device="cuda:0", seed=m + 1)
+            for m in range(M)]
+    res = AP.measure(ffns, xs, attn, layers=layers, reps=3)
+    assert res["outputs_identical"]
+
+    hb = [xi.clone() for xi in xs]
+    ab = [torch.empty_like(xi) for xi in xs]
+    for _ in range(layers):
+        for m in range(M):
+            attn[m].forward(hb[m], ab[m])
+            ffns[m].forward(ab[m], out=hb[m])
+    torch.cuda.synchronize()
+    for m in range(M):
+        assert torch.isfinite(hb[m].float()).all()
+        assert torch.equal(hb[m], res["finals"]["serial"][m])
+    assert set(res["period_ms"]) == {"serial", "overlap", "split"}
+    assert all(v > 0 for v in res["period_ms"].values())
+    assert res["split"]["attn_cus"] + res["split"]["ffn_cus"] == res["num_cus"]
