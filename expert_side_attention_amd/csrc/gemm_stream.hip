@@ -16,7 +16,11 @@
 //    q = lane/16 takes 16 bytes at 64 i + 16 q), so every instruction moves
 //    whole 64-byte row segments.
 //  * The gathered activation rows (a few KB per tile, shared by all waves)
-//    are staged through LDS, double-buffered per super-stage.
+//    are staged through LDS, double-buffered per super-stage.  The bf16
+//    down GEMMs load them two super-stages ahead, so that storing them to
+//    LDS never waits on a load issued in the same stage; the other shapes
+//    load them one stage ahead (two would spill registers or, in fp8, cost
+//    more than it saves).
 //  * bf16: chunk i is one 16x16x32 MFMA.  fp8: chunks 2b and 2b+1 (bytes
 //    [128 b + 16 q] and [128 b + 64 + 16 q]) lie in the same 128-wide K
 //    block b and feed one 16x16x128 MFMA; the block's partial sum is then
@@ -76,14 +80,15 @@ struct StreamCfg {
 // K (in bytes per row) must be a multiple of SS for every group; the
 // launcher picks an instantiation that satisfies this, so the main loop has
 // no partial super-stage and no per-load guard.
-template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
+// AD: how many super-stages ahead the activation rows are loaded (1 or 2).
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU, int AD>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void stream_gemm_kernel(const GemmArgs p) {
   using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU>;
   constexpr int NMAT = C::NMAT, BN = C::BN, MB = C::MB, NPR = C::NPR;
   constexpr int APITCH = C::APITCH, CPR = C::CPR, RPP = C::RPP, RA = C::RA, KB = C::KB;
-  constexpr int SKB = C::FP8 ? KB : 1;
 
   __shared__ __align__(16) uint8_t lds[C::LDS];
+  static_assert(AD == 1 || AD == 2, "activation prefetch distance");
   // fp8: activation scale x weight block scale, [buffer][matrix][K block][row]
   __shared__ __align__(16) float sAs[2][NMAT][C::FP8 ? KB : 1][C::FP8 ? BM : 4];
   __shared__ int s_item;
@@ -157,17 +162,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     // two bf16 MFMA operands
     u32x8 bq[2][NMAT][NPR];
     float sbq[2][NMAT][C::FP8 ? KB : 1];
-    u32x4 ra[RA];
-    float as_reg = 0.0f;
-    // order of issue per super-stage: A rows, A scales, B scales, B rows.
-    // Vector loads complete in order, so the waits for one stage's A leave
-    // the same stage's B in flight.
-    auto load_a = [&](int ss) {
+    // activation rows and scales of AD super-stages, slot = stage % AD
+    u32x4 ra[AD][RA];
+    float as_reg[AD] = {};
+    // order of issue: A rows, A scales, B scales, B rows.  Vector loads
+    // complete in order, so a wait for A leaves the B rows issued after it
+    // in flight.
+    auto load_a = [&](auto slot_c, int ss) {
+      constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
       for (int i = 0; i < RA; ++i)
-        ra[i] = ld16(abase_g + static_cast<int64_t>(asrc[i]) * p.a_pitch +
-                     static_cast<int64_t>(ss) * SS);
-      if constexpr (C::FP8) as_reg = asc[ss * KB];
+        ra[SL][i] = ld16(abase_g + static_cast<int64_t>(asrc[i]) * p.a_pitch +
+                         static_cast<int64_t>(ss) * SS);
+      if constexpr (C::FP8) as_reg[SL] = asc[ss * KB];
     };
     auto load_b = [&](u32x8 (&dst)[NMAT][NPR], float (&sdst)[NMAT][C::FP8 ? KB : 1], int ss) {
       if constexpr (C::FP8) {
@@ -185,12 +192,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
           dst[m][c].hi = ld16(src + 64);
         }
     };
-    // sb: the B scales of the same stage (their loads were issued before
-    // the B rows, so waiting for them leaves the B rows in flight)
-    auto store_a = [&](int buf, const float (&sb)[NMAT][SKB]) {
+    // sb: the B scales of the stored stage (fp8; their loads were issued
+    // before the B rows, so waiting for them leaves the B rows in flight)
+    auto store_a = [&](int buf, auto slot_c, const float (&sb)[NMAT][C::FP8 ? KB : 1]) {
+      constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
       for (int i = 0; i < RA; ++i)
-        st16(lds + buf * BM * APITCH + (arow0 + i * RPP) * APITCH + acol * 16, ra[i]);
+        st16(lds + buf * BM * APITCH + (arow0 + i * RPP) * APITCH + acol * 16, ra[SL][i]);
       if constexpr (C::FP8)
         if (tid < BM * KB) {
           const int kb = tid % KB;
@@ -200,11 +208,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
             // select the block without dynamic register indexing
             float v = sb[m][0];
 #pragma unroll
-            for (int k2 = 1; k2 < SKB; ++k2) v = kb == k2 ? sb[m][k2] : v;
+            for (int k2 = 1; k2 < KB; ++k2) v = kb == k2 ? sb[m][k2] : v;
             sbk[m] = v;
           }
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) sAs[buf][m][kb][tid / KB] = as_reg * sbk[m];
+          for (int m = 0; m < NMAT; ++m) sAs[buf][m][kb][tid / KB] = as_reg[SL] * sbk[m];
         }
     };
 
@@ -261,20 +269,34 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
       }
     };
 
-    // ---- pipeline: B one super-stage ahead in registers, A double-buffered
-    // in LDS.  The last stage is peeled so that every prefetch in the loop is
-    // unconditional: a load behind a branch would make the wait before the
-    // next MFMA cover the loads just issued.
-    load_a(0);
+    // ---- pipeline: B one super-stage ahead in registers, A AD stages ahead
+    // in registers and double-buffered in LDS.  The last stage is peeled so
+    // that every prefetch in the loop is unconditional: a load behind a
+    // branch would make the wait before the next MFMA cover the loads just
+    // issued.  With AD = 2 the rows stored after a stage's math were loaded
+    // before that stage's weights, so the store never waits on a load issued
+    // in the same stage (prefetches past the last stage re-read it); fp8
+    // keeps AD = 1, as its store also needs the B scales loaded in the stage.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, AD - 1>;
+    load_a(S0{}, 0);
+    if constexpr (AD == 2) load_a(S1{}, nss > 1 ? 1 : 0);
     load_b(bq[0], sbq[0], 0);
-    store_a(0, sbq[0]);
+    store_a(0, S0{}, sbq[0]);
     __syncthreads();
     auto step = [&](auto par, int ss) {  // ss + 1 < nss
       constexpr int P = decltype(par)::value;  // == ss & 1
-      load_a(ss + 1);
-      load_b(bq[P ^ 1], sbq[P ^ 1], ss + 1);
-      compute(bq[P], sbq[P], P);
-      store_a(P ^ 1, sbq[P ^ 1]);
+      if constexpr (AD == 2) {
+        load_a(std::integral_constant<int, P>{}, ss + 2 < nss ? ss + 2 : nss - 1);
+        load_b(bq[P ^ 1], sbq[P ^ 1], ss + 1);
+        compute(bq[P], sbq[P], P);
+        store_a(P ^ 1, std::integral_constant<int, P ^ 1>{}, sbq[P ^ 1]);
+      } else {
+        load_a(S0{}, ss + 1);
+        load_b(bq[P ^ 1], sbq[P ^ 1], ss + 1);
+        compute(bq[P], sbq[P], P);
+        store_a(P ^ 1, S0{}, sbq[P ^ 1]);
+      }
       __syncthreads();
     };
     int ss = 0;
@@ -378,9 +400,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   }
 }
 
-template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU, int AD = 1>
 hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
-  auto kern = stream_gemm_kernel<EL, WAVES, BM, SS, SWIGLU>;
+  auto kern = stream_gemm_kernel<EL, WAVES, BM, SS, SWIGLU, AD>;
   // resident workgroups of this kernel on the current device (cached per device)
   constexpr int kMaxDevices = 64;
   static std::atomic<int> resident[kMaxDevices];
@@ -425,13 +447,13 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
       if (gu)
         return fits(512) ? launch_stream<Elem::BF16, 4, 64, 512, true>(a, s)
                          : launch_stream<Elem::BF16, 4, 64, 128, true>(a, s);
-      return launch_stream<Elem::BF16, 8, 64, 256, false>(a, s);
+      return launch_stream<Elem::BF16, 8, 64, 256, false, 2>(a, s);
     }
     if (bm == 128) {
       if (gu)
         return fits(256) ? launch_stream<Elem::BF16, 4, 128, 256, true>(a, s)
                          : launch_stream<Elem::BF16, 4, 128, 128, true>(a, s);
-      return fits(256) ? launch_stream<Elem::BF16, 8, 128, 256, false>(a, s)
+      return fits(256) ? launch_stream<Elem::BF16, 8, 128, 256, false, 2>(a, s)
                        : launch_stream<Elem::BF16, 8, 128, 128, false>(a, s);
     }
   } else if (elem == 2) {
