@@ -16,11 +16,11 @@
 //    q = lane/16 takes 16 bytes at 64 i + 16 q), so every instruction moves
 //    whole 64-byte row segments.
 //  * The gathered activation rows (a few KB per tile, shared by all waves)
-//    are staged through LDS, double-buffered per super-stage.  The bf16
-//    down GEMMs load them two super-stages ahead, so that storing them to
-//    LDS never waits on a load issued in the same stage; the other shapes
-//    load them one stage ahead (two would spill registers or, in fp8, cost
-//    more than it saves).
+//    are staged through LDS, double-buffered per super-stage.  The down
+//    GEMMs load them (and in fp8 the scales the store needs) two
+//    super-stages ahead, so that storing them to LDS never waits on a load
+//    issued in the same stage; the gate/up shapes load them one stage ahead
+//    (two spill registers in bf16 and are slower in fp8).
 //  * bf16: chunk i is one 16x16x32 MFMA.  fp8: chunks 2b and 2b+1 (bytes
 //    [128 b + 16 q] and [128 b + 64 + 16 q]) lie in the same 128-wide K
 //    block b and feed one 16x16x128 MFMA; the block's partial sum is then
@@ -161,28 +161,30 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     // (bytes [128 c + 16 q] and [128 c + 64 + 16 q]), one fp8 MFMA operand or
     // two bf16 MFMA operands
     u32x8 bq[2][NMAT][NPR];
-    float sbq[2][NMAT][C::FP8 ? KB : 1];
-    // activation rows and scales of AD super-stages, slot = stage % AD
+    // what the LDS store of AD super-stages needs, slot = stage % AD:
+    // activation rows, and in fp8 the activation scale and the B block
+    // scales (the store writes their product)
     u32x4 ra[AD][RA];
     float as_reg[AD] = {};
-    // order of issue: A rows, A scales, B scales, B rows.  Vector loads
-    // complete in order, so a wait for A leaves the B rows issued after it
-    // in flight.
+    float sbs[AD][NMAT][C::FP8 ? KB : 1];
+    // order of issue: A rows, A scale, B scales, then the B rows of a stage.
+    // Vector loads complete in order, so a wait for the first three leaves
+    // the B rows issued after them in flight.
     auto load_a = [&](auto slot_c, int ss) {
       constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
       for (int i = 0; i < RA; ++i)
         ra[SL][i] = ld16(abase_g + static_cast<int64_t>(asrc[i]) * p.a_pitch +
                          static_cast<int64_t>(ss) * SS);
-      if constexpr (C::FP8) as_reg[SL] = asc[ss * KB];
-    };
-    auto load_b = [&](u32x8 (&dst)[NMAT][NPR], float (&sdst)[NMAT][C::FP8 ? KB : 1], int ss) {
       if constexpr (C::FP8) {
+        as_reg[SL] = asc[ss * KB];
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) sdst[m][kb] = bsc[m][ss * KB + kb];
+          for (int kb = 0; kb < KB; ++kb) sbs[SL][m][kb] = bsc[m][ss * KB + kb];
       }
+    };
+    auto load_b = [&](u32x8 (&dst)[NMAT][NPR], int ss) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -192,10 +194,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
           dst[m][c].hi = ld16(src + 64);
         }
     };
-    // sb: the B scales of the stored stage (fp8; their loads were issued
-    // before the B rows, so waiting for them leaves the B rows in flight)
-    auto store_a = [&](int buf, auto slot_c, const float (&sb)[NMAT][C::FP8 ? KB : 1]) {
+    auto store_a = [&](int buf, auto slot_c) {
       constexpr int SL = decltype(slot_c)::value;
+      const float (&sb)[NMAT][C::FP8 ? KB : 1] = sbs[SL];
 #pragma unroll
       for (int i = 0; i < RA; ++i)
         st16(lds + buf * BM * APITCH + (arow0 + i * RPP) * APITCH + acol * 16, ra[SL][i]);
@@ -222,8 +223,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[m][b] = f32x4{0, 0, 0, 0};
 
-    auto compute = [&](const u32x8 (&bb)[NMAT][NPR], const float (&sb)[NMAT][C::FP8 ? KB : 1],
-                       int buf) {
+    auto compute = [&](const u32x8 (&bb)[NMAT][NPR], int buf) {
       const uint8_t *abase = lds + buf * BM * APITCH + r16 * APITCH + q * 16;
       if constexpr (!C::FP8) {
 #pragma unroll
@@ -273,29 +273,28 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     // in registers and double-buffered in LDS.  The last stage is peeled so
     // that every prefetch in the loop is unconditional: a load behind a
     // branch would make the wait before the next MFMA cover the loads just
-    // issued.  With AD = 2 the rows stored after a stage's math were loaded
+    // issued.  With AD = 2 what is stored after a stage's math was loaded
     // before that stage's weights, so the store never waits on a load issued
-    // in the same stage (prefetches past the last stage re-read it); fp8
-    // keeps AD = 1, as its store also needs the B scales loaded in the stage.
+    // in the same stage (prefetches past the last stage re-read it).
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, AD - 1>;
     load_a(S0{}, 0);
     if constexpr (AD == 2) load_a(S1{}, nss > 1 ? 1 : 0);
-    load_b(bq[0], sbq[0], 0);
-    store_a(0, S0{}, sbq[0]);
+    load_b(bq[0], 0);
+    store_a(0, S0{});
     __syncthreads();
     auto step = [&](auto par, int ss) {  // ss + 1 < nss
       constexpr int P = decltype(par)::value;  // == ss & 1
       if constexpr (AD == 2) {
         load_a(std::integral_constant<int, P>{}, ss + 2 < nss ? ss + 2 : nss - 1);
-        load_b(bq[P ^ 1], sbq[P ^ 1], ss + 1);
-        compute(bq[P], sbq[P], P);
-        store_a(P ^ 1, std::integral_constant<int, P ^ 1>{}, sbq[P ^ 1]);
+        load_b(bq[P ^ 1], ss + 1);
+        compute(bq[P], P);
+        store_a(P ^ 1, std::integral_constant<int, P ^ 1>{});
       } else {
         load_a(S0{}, ss + 1);
-        load_b(bq[P ^ 1], sbq[P ^ 1], ss + 1);
-        compute(bq[P], sbq[P], P);
-        store_a(P ^ 1, S0{}, sbq[P ^ 1]);
+        load_b(bq[P ^ 1], ss + 1);
+        compute(bq[P], P);
+        store_a(P ^ 1, S0{});
       }
       __syncthreads();
     };
@@ -306,9 +305,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     }
     if (ss + 1 < nss) {
       step(std::integral_constant<int, 0>{}, ss);
-      compute(bq[1], sbq[1], 1);
+      compute(bq[1], 1);
     } else {
-      compute(bq[0], sbq[0], 0);
+      compute(bq[0], 0);
     }
     __syncthreads();
 
@@ -467,7 +466,7 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
       // both gate/up shapes are 128 columns wide: stream_gate_up_writes_fp8
       return gu ? (fits(256) ? launch_stream<Elem::FP8, 8, 128, 256, true>(a, s)
                           : launch_stream<Elem::FP8, 8, 128, 128, true>(a, s))
-                : launch_stream<Elem::FP8, 8, 128, 128, false>(a, s);
+                : launch_stream<Elem::FP8, 8, 128, 128, false, 2>(a, s);
   }
   return hipErrorInvalidValue;
 }
