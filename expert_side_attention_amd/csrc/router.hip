@@ -225,9 +225,10 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   }
   const uint16_t *X = static_cast<const uint16_t *>(x);
   const uint16_t *W = static_cast<const uint16_t *>(wr);
-  // token blocks of 16 (64 above 1024 tokens), expert slices sized so that a
-  // batch launches a few hundred workgroups, K split over 8 waves (4 for the
-  // 64-token blocks, whose partial sums would not fit LDS otherwise)
+  // token blocks of 16 (32 up to 4096 tokens, 64 above), expert slices sized
+  // so that a batch launches a few hundred workgroups, K split over 8 waves
+  // (4 for the 64-token blocks, whose partial sums would not fit LDS
+  // otherwise)
 #define AFD_ROUTER(TM, EN, NBUF, WAVES)                                                 \
   router_bf16_kernel<TM, EN, NBUF, WAVES>                                              \
       <<<dim3((E + EN - 1) / EN, (T + TM - 1) / TM), WAVES * 64, 0, s>>>(X, W, bias, T, h, \
@@ -238,17 +239,17 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   if (E > 256) {
     if (k8) AFD_ROUTER(16, 64, 4, 8);
     else AFD_ROUTER(16, 64, 4, 4);
-  } else if (T > 1024) {
+  } else if (T > 4096) {
     AFD_ROUTER(64, 64, 4, 4);
+  } else if (T > 1024) {
+    if (k8) AFD_ROUTER(32, 64, 4, 8);
+    else AFD_ROUTER(32, 64, 4, 4);
   } else if (E <= 64 || T <= 256) {
     if (k8) AFD_ROUTER(16, 16, 8, 8);
     else AFD_ROUTER(16, 16, 8, 4);
-  } else if (T <= 1024) {
+  } else {
     if (k8) AFD_ROUTER(16, 32, 6, 8);
     else AFD_ROUTER(16, 32, 6, 4);
-  } else {
-    if (k8) AFD_ROUTER(16, 64, 4, 8);
-    else AFD_ROUTER(16, 64, 4, 4);
   }
 #undef AFD_ROUTER
   hipError_t e = hipGetLastError();
