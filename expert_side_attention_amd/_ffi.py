@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "afd_ffn_destroy": (None, [P]),
         "afd_quant_fp8_1x128": (ctypes.c_int, [P, I64, I64, P, P, P]),
         "afd_quant_fp8_128x128": (ctypes.c_int, [P, I64, I64, P, P, P]),
+        "afd_quant_fp8_1x128_f32": (ctypes.c_int, [P, I64, I64, P, P, P]),
         "afd_ffn_profile_enable": (ctypes.c_int, [P, U32]),
         "afd_ffn_profile_read": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_int64)]),
@@ -124,6 +125,10 @@ def afd_ffn_destroy(h):
 
 def afd_quant_fp8_1x128(x: int, rows: int, cols: int, q: int, s: int, stream: int):
     _check(load_library().afd_quant_fp8_1x128(x, rows, cols, q, s, stream))
+
+
+def afd_quant_fp8_1x128_f32(x: int, rows: int, cols: int, q: int, s: int, stream: int):
+    _check(load_library().afd_quant_fp8_1x128_f32(x, rows, cols, q, s, stream))
 
 
 def afd_quant_fp8_128x128(w: int, rows: int, cols: int, q: int, s: int, stream: int):

@@ -474,6 +474,19 @@ int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols, uint8_t *q, f
   return e == hipSuccess ? AFD_OK : hip_fail(e, "quantiser launch");
 }
 
+int afd_quant_fp8_1x128_f32(const float *x, int64_t rows, int64_t cols, uint8_t *q, float *s,
+                            afd_stream_t stream) {
+  if (!x || !q || !s) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");
+  if (rows < 0 || cols <= 0 || cols % 128)
+    return fail(AFD_ERR_INVALID_ARG, "rows >= 0 and cols a positive multiple of 128 required");
+  if (rows == 0) return AFD_OK;
+  if (rows * (cols / 128) * 16 / 256 >= (1LL << 31))
+    return fail(AFD_ERR_UNSUPPORTED, "tensor too large for one launch");
+  hipError_t e = afd::launch_quant_1x128_f32(x, rows, cols, cols, q, cols, s, cols / 128,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AFD_OK : hip_fail(e, "quantiser launch");
+}
+
 int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols, uint8_t *q, float *s,
                           afd_stream_t stream) {
   if (!w || !q || !s) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");

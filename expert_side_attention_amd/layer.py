@@ -37,14 +37,15 @@ def _need(t, name, dtype, shape, device):
 
 
 def quantize_fp8_1x128(x: torch.Tensor, stream=None):
-    """E4M3 codes (uint8) and fp32 scales [rows, cols/128] of a bf16 matrix."""
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D bf16 tensor")
+    """E4M3 codes (uint8) and fp32 scales [rows, cols/128] of a bf16 or fp32
+    matrix."""
+    if x.dtype not in (torch.bfloat16, torch.float32) or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bf16 or fp32 tensor")
     rows, cols = x.shape
     q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     s = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
-    F.afd_quant_fp8_1x128(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
-                          _stream(stream))
+    fn = F.afd_quant_fp8_1x128 if x.dtype == torch.bfloat16 else F.afd_quant_fp8_1x128_f32
+    fn(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(), _stream(stream))
     return q, s
 
 

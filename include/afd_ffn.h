@@ -156,6 +156,15 @@ void afd_ffn_destroy(afd_ffn_handle *h);
 int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols,
                         uint8_t *q, float *s, afd_stream_t stream);
 
+/* The same quantiser on fp32 input: the W8A8 layer applies it to the
+ * SwiGLU output z between the two expert GEMMs (W8A8 is the precision of
+ * the vLLM AFD plugin page's "效能基準測試").  x [rows, cols]
+ * fp32 device array, row-major, contiguous; q, s as above; all three owned
+ * by the caller.  Errors: NULL pointer or cols not a positive multiple of
+ * 128 -> AFD_ERR_INVALID_ARG; rows = 0 is a no-op.                        */
+int afd_quant_fp8_1x128_f32(const float *x, int64_t rows, int64_t cols,
+                            uint8_t *q, float *s, afd_stream_t stream);
+
 /* FP8 E4M3 weight quantiser: one scale per 128x128 block, same rounding.
  * w [rows, cols] bf16 -> q [rows, cols], s [rows/128, cols/128].
  * rows % 128 == 0, cols % 128 == 0.  A stack [E, N, K] is rows = E*N.     */

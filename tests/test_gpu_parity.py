@@ -281,3 +281,38 @@ def test_block_quantiser_matches_oracle():
         rq, rs = O.quantize_128x128(O.bf16_to_f64(wb[e]).astype(np.float32))
         assert np.array_equal(q[e].cpu().numpy(), rq)
         assert np.array_equal(s[e].cpu().numpy(), rs)
+
+
+def test_fp32_encoder_every_value_in_range():
+    """The fp32 1x128 quantiser (the one W8A8 applies to z) on every fp32
+    value from 2^-10 (below it everything rounds to zero) to 448, both signs,
+    plus a sample of smaller ones: each group of 128 holds 448 and 127 test
+    values, so its scale is exactly 1 and every code is the encoding of the
+    value itself.  Codes and scales bit-exact against the oracle."""
+    from expert_side_attention_amd import quantize_fp8_1x128
+    lo_field, hi_field = 117, 135            # fp32 exponent fields of 2^-10 .. 2^8
+    m448 = 0x600000                          # 448 = 1.75 * 2^8
+    chunks = []
+    for f in range(lo_field, hi_field + 1):
+        m = np.arange((m448 + 1) if f == hi_field else (1 << 23), dtype=np.uint32)
+        chunks.append((np.uint32(f) << np.uint32(23)) | m)
+    small = np.random.default_rng(3).integers(0, lo_field << 23, 1 << 20, dtype=np.uint32)
+    chunks.append(small)
+    checked = 0
+    for c in chunks:
+        for sign in (0, 1):
+            bits = c | np.uint32(sign << 31)
+            n = -(-bits.size // 127)
+            vals = np.zeros(n * 127, np.uint32)
+            vals[: bits.size] = bits
+            x = np.empty((n, 128), np.float32)
+            x[:, 0] = 448.0
+            x[:, 1:] = vals.view(np.float32).reshape(n, 127)
+            q, s = quantize_fp8_1x128(torch.from_numpy(x).to(DEV))
+            torch.cuda.synchronize()
+            rq, rs = O.quantize_1x128(x)
+            assert np.all(rs == 1.0)
+            assert np.array_equal(s.cpu().numpy(), rs)
+            assert np.array_equal(q.cpu().numpy(), rq), f"chunk starting {bits[0]:#x}"
+            checked += bits.size
+    assert checked > 300_000_000
