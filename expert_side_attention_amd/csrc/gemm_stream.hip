@@ -125,276 +125,301 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
       const int r = tile.row0 + (row < rows ? row : 0);
       return p.perm ? (r < p.Tk ? p.perm[r] : (r - p.Tk) % p.T) : r;
     };
-    int asrc[RA];
-#pragma unroll
-    for (int i = 0; i < RA; ++i) asrc[i] = source_row(arow0 + i * RPP);
-    const uint8_t *abase_g = p.A + acol * 16;
-    // activation scales: thread tid < BM * KB stages scale (row tid / KB,
-    // block tid % KB); the others load a valid address and drop the value,
-    // so every load of the main loop is unconditional
-    const float *asc = p.a_scale;
-    if constexpr (C::FP8) {
-      const int as_t = tid < BM * KB ? tid : 0;
-      asc = p.a_scale + static_cast<int64_t>(source_row(as_t / KB)) * p.a_scale_pitch + as_t % KB;
-    }
-
-    const int64_t mat = static_cast<int64_t>(N) * krow;
-    const uint8_t *bptr[NMAT];
-    {
-      const uint8_t *b0 = (shared ? p.sb0 : p.b0) + g * mat;
-      bptr[0] = b0 + static_cast<int64_t>(n0 + wave * 16 + r16) * krow + q * 16;
-      if constexpr (SWIGLU) {
-        const uint8_t *b1 = (shared ? p.sb1 : p.b1) + g * mat;
-        bptr[NMAT - 1] = b1 + static_cast<int64_t>(n0 + wave * 16 + r16) * krow + q * 16;
-      }
-    }
-    const float *bsc[NMAT] = {};
-    if constexpr (C::FP8) {
-      const int kblocks = K / 128;
-      const int64_t sblk = static_cast<int64_t>(N / 128) * kblocks;
-      bsc[0] = (shared ? p.sbs0 : p.bs0) + g * sblk + (n0 / 128) * kblocks;
-      if constexpr (SWIGLU) bsc[NMAT - 1] = (shared ? p.sbs1 : p.bs1) + g * sblk + (n0 / 128) * kblocks;
-    }
-    const int mb_active = (rows + 15) >> 4;
-
-    // ---- registers: 128-byte K piece c of a row block is one 8-dword tuple
-    // (bytes [128 c + 16 q] and [128 c + 64 + 16 q]), one fp8 MFMA operand or
-    // two bf16 MFMA operands
-    u32x8 bq[2][NMAT][NPR];
-    // what the LDS store of AD super-stages needs, slot = stage % AD:
-    // activation rows, and in fp8 the activation scale and the B block
-    // scales (the store writes their product)
-    u32x4 ra[AD][RA];
-    float as_reg[AD] = {};
-    float sbs[AD][NMAT][C::FP8 ? KB : 1];
-    // order of issue: A rows, A scale, B scales, then the B rows of a stage.
-    // Vector loads complete in order, so a wait for the first three leaves
-    // the B rows issued after them in flight.
-    auto load_a = [&](auto slot_c, int ss) {
-      constexpr int SL = decltype(slot_c)::value;
-#pragma unroll
-      for (int i = 0; i < RA; ++i)
-        ra[SL][i] = ld16(abase_g + static_cast<int64_t>(asrc[i]) * p.a_pitch +
-                         static_cast<int64_t>(ss) * SS);
+    // The item body, for RAX staging passes of the A rows (the passes that
+    // hold rows of this tile) and activation prefetch distance ADX.  Tiles
+    // that fill half or a quarter of the passes stage only those and, with
+    // the staging registers that frees, load the rows two stages ahead.
+    auto body = [&](auto rax_c, auto adx_c) {
+      constexpr int RAX = decltype(rax_c)::value;
+      constexpr int ADX = decltype(adx_c)::value;
+      // the staged rows cover every active 16-row MFMA block
+      static_assert((RAX * RPP) % 16 == 0, "staged rows are whole row blocks");
+      int asrc[RAX];
+  #pragma unroll
+      for (int i = 0; i < RAX; ++i) asrc[i] = source_row(arow0 + i * RPP);
+      const uint8_t *abase_g = p.A + acol * 16;
+      // activation scales: thread tid < BM * KB stages scale (row tid / KB,
+      // block tid % KB); the others load a valid address and drop the value,
+      // so every load of the main loop is unconditional
+      const float *asc = p.a_scale;
       if constexpr (C::FP8) {
-        as_reg[SL] = asc[ss * KB];
-#pragma unroll
+        const int as_t = tid < BM * KB ? tid : 0;
+        asc = p.a_scale + static_cast<int64_t>(source_row(as_t / KB)) * p.a_scale_pitch + as_t % KB;
+      }
+
+      const int64_t mat = static_cast<int64_t>(N) * krow;
+      const uint8_t *bptr[NMAT];
+      {
+        const uint8_t *b0 = (shared ? p.sb0 : p.b0) + g * mat;
+        bptr[0] = b0 + static_cast<int64_t>(n0 + wave * 16 + r16) * krow + q * 16;
+        if constexpr (SWIGLU) {
+          const uint8_t *b1 = (shared ? p.sb1 : p.b1) + g * mat;
+          bptr[NMAT - 1] = b1 + static_cast<int64_t>(n0 + wave * 16 + r16) * krow + q * 16;
+        }
+      }
+      const float *bsc[NMAT] = {};
+      if constexpr (C::FP8) {
+        const int kblocks = K / 128;
+        const int64_t sblk = static_cast<int64_t>(N / 128) * kblocks;
+        bsc[0] = (shared ? p.sbs0 : p.bs0) + g * sblk + (n0 / 128) * kblocks;
+        if constexpr (SWIGLU) bsc[NMAT - 1] = (shared ? p.sbs1 : p.bs1) + g * sblk + (n0 / 128) * kblocks;
+      }
+      const int mb_active = (rows + 15) >> 4;
+
+      // ---- registers: 128-byte K piece c of a row block is one 8-dword tuple
+      // (bytes [128 c + 16 q] and [128 c + 64 + 16 q]), one fp8 MFMA operand or
+      // two bf16 MFMA operands
+      u32x8 bq[2][NMAT][NPR];
+      // what the LDS store of ADX super-stages needs, slot = stage % ADX:
+      // activation rows, and in fp8 the activation scale and the B block
+      // scales (the store writes their product)
+      u32x4 ra[ADX][RAX];
+      float as_reg[ADX] = {};
+      float sbs[ADX][NMAT][C::FP8 ? KB : 1];
+      // order of issue: A rows, A scale, B scales, then the B rows of a stage.
+      // Vector loads complete in order, so a wait for the first three leaves
+      // the B rows issued after them in flight.
+      auto load_a = [&](auto slot_c, int ss) {
+        constexpr int SL = decltype(slot_c)::value;
+  #pragma unroll
+        for (int i = 0; i < RAX; ++i)
+          ra[SL][i] = ld16(abase_g + static_cast<int64_t>(asrc[i]) * p.a_pitch +
+                           static_cast<int64_t>(ss) * SS);
+        if constexpr (C::FP8) {
+          as_reg[SL] = asc[ss * KB];
+  #pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+  #pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sbs[SL][m][kb] = bsc[m][ss * KB + kb];
+        }
+      };
+      auto load_b = [&](u32x8 (&dst)[NMAT][NPR], int ss) {
+  #pragma unroll
         for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) sbs[SL][m][kb] = bsc[m][ss * KB + kb];
-      }
-    };
-    auto load_b = [&](u32x8 (&dst)[NMAT][NPR], int ss) {
-#pragma unroll
+  #pragma unroll
+          for (int c = 0; c < NPR; ++c) {
+            const uint8_t *src = bptr[m] + static_cast<int64_t>(ss) * SS + c * 128;
+            dst[m][c].lo = ld16(src);
+            dst[m][c].hi = ld16(src + 64);
+          }
+      };
+      auto store_a = [&](int buf, auto slot_c) {
+        constexpr int SL = decltype(slot_c)::value;
+        const float (&sb)[NMAT][C::FP8 ? KB : 1] = sbs[SL];
+  #pragma unroll
+        for (int i = 0; i < RAX; ++i)
+          st16(lds + buf * BM * APITCH + (arow0 + i * RPP) * APITCH + acol * 16, ra[SL][i]);
+        if constexpr (C::FP8)
+          if (tid < BM * KB) {
+            const int kb = tid % KB;
+            float sbk[NMAT];
+  #pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+              // select the block without dynamic register indexing
+              float v = sb[m][0];
+  #pragma unroll
+              for (int k2 = 1; k2 < KB; ++k2) v = kb == k2 ? sb[m][k2] : v;
+              sbk[m] = v;
+            }
+  #pragma unroll
+            for (int m = 0; m < NMAT; ++m) sAs[buf][m][kb][tid / KB] = as_reg[SL] * sbk[m];
+          }
+      };
+
+      f32x4 acc[NMAT][MB];
+  #pragma unroll
       for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int c = 0; c < NPR; ++c) {
-          const uint8_t *src = bptr[m] + static_cast<int64_t>(ss) * SS + c * 128;
-          dst[m][c].lo = ld16(src);
-          dst[m][c].hi = ld16(src + 64);
-        }
-    };
-    auto store_a = [&](int buf, auto slot_c) {
-      constexpr int SL = decltype(slot_c)::value;
-      const float (&sb)[NMAT][C::FP8 ? KB : 1] = sbs[SL];
-#pragma unroll
-      for (int i = 0; i < RA; ++i)
-        st16(lds + buf * BM * APITCH + (arow0 + i * RPP) * APITCH + acol * 16, ra[SL][i]);
-      if constexpr (C::FP8)
-        if (tid < BM * KB) {
-          const int kb = tid % KB;
-          float sbk[NMAT];
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m) {
-            // select the block without dynamic register indexing
-            float v = sb[m][0];
-#pragma unroll
-            for (int k2 = 1; k2 < KB; ++k2) v = kb == k2 ? sb[m][k2] : v;
-            sbk[m] = v;
-          }
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m) sAs[buf][m][kb][tid / KB] = as_reg[SL] * sbk[m];
-        }
-    };
+  #pragma unroll
+        for (int b = 0; b < MB; ++b) acc[m][b] = f32x4{0, 0, 0, 0};
 
-    f32x4 acc[NMAT][MB];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int b = 0; b < MB; ++b) acc[m][b] = f32x4{0, 0, 0, 0};
-
-    auto compute = [&](const u32x8 (&bb)[NMAT][NPR], int buf) {
-      const uint8_t *abase = lds + buf * BM * APITCH + r16 * APITCH + q * 16;
-      if constexpr (!C::FP8) {
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-          if (b < mb_active) {
-#pragma unroll
-            for (int c = 0; c < NPR; ++c) {
-              const u32x4 a0 = ld16(abase + b * 16 * APITCH + c * 128);
-              const u32x4 a1 = ld16(abase + b * 16 * APITCH + c * 128 + 64);
-#pragma unroll
-              for (int m = 0; m < NMAT; ++m) {
-                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a0), bitcast<bf16x8>(bb[m][c].lo), acc[m][b]);
-                acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a1), bitcast<bf16x8>(bb[m][c].hi), acc[m][b]);
+      auto compute = [&](const u32x8 (&bb)[NMAT][NPR], int buf) {
+        const uint8_t *abase = lds + buf * BM * APITCH + r16 * APITCH + q * 16;
+        if constexpr (!C::FP8) {
+  #pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            if (b < mb_active) {
+  #pragma unroll
+              for (int c = 0; c < NPR; ++c) {
+                const u32x4 a0 = ld16(abase + b * 16 * APITCH + c * 128);
+                const u32x4 a1 = ld16(abase + b * 16 * APITCH + c * 128 + 64);
+  #pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                  acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a0), bitcast<bf16x8>(bb[m][c].lo), acc[m][b]);
+                  acc[m][b] = mfma_bf16_k32(bitcast<bf16x8>(a1), bitcast<bf16x8>(bb[m][c].hi), acc[m][b]);
+                }
               }
             }
+            // bound the A reads the compiler hoists to one row block
+            __builtin_amdgcn_sched_barrier(0);
           }
-          // bound the A reads the compiler hoists to one row block
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-          if (b < mb_active) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              u32x8 a;
-              a.lo = ld16(abase + b * 16 * APITCH + kb * 128);
-              a.hi = ld16(abase + b * 16 * APITCH + kb * 128 + 64);
-#pragma unroll
-              for (int m = 0; m < NMAT; ++m) {
-                const f32x4 sab = *reinterpret_cast<const f32x4 *>(&sAs[buf][m][kb][b * 16 + q * 4]);
-                const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, bb[m][kb]),
-                    f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[m][b][i] = fmaf(part[i], sab[i], acc[m][b][i]);
+        } else {
+  #pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            if (b < mb_active) {
+  #pragma unroll
+              for (int kb = 0; kb < KB; ++kb) {
+                u32x8 a;
+                a.lo = ld16(abase + b * 16 * APITCH + kb * 128);
+                a.hi = ld16(abase + b * 16 * APITCH + kb * 128 + 64);
+  #pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                  const f32x4 sab = *reinterpret_cast<const f32x4 *>(&sAs[buf][m][kb][b * 16 + q * 4]);
+                  const f32x4 part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                      __builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, bb[m][kb]),
+                      f32x4{0, 0, 0, 0}, 0, 0, 0, 127, 0, 127);
+  #pragma unroll
+                  for (int i = 0; i < 4; ++i) acc[m][b][i] = fmaf(part[i], sab[i], acc[m][b][i]);
+                }
               }
             }
+            // keep the partial sums of one row block live at a time
+            __builtin_amdgcn_sched_barrier(0);
           }
-          // keep the partial sums of one row block live at a time
-          __builtin_amdgcn_sched_barrier(0);
         }
+      };
+
+      // ---- pipeline: B one super-stage ahead in registers, A ADX stages ahead
+      // in registers and double-buffered in LDS.  The last stage is peeled so
+      // that every prefetch in the loop is unconditional: a load behind a
+      // branch would make the wait before the next MFMA cover the loads just
+      // issued.  With ADX = 2 what is stored after a stage's math was loaded
+      // before that stage's weights, so the store never waits on a load issued
+      // in the same stage (prefetches past the last stage re-read it).
+      using S0 = std::integral_constant<int, 0>;
+      using S1 = std::integral_constant<int, ADX - 1>;
+      load_a(S0{}, 0);
+      if constexpr (ADX == 2) load_a(S1{}, nss > 1 ? 1 : 0);
+      load_b(bq[0], 0);
+      store_a(0, S0{});
+      __syncthreads();
+      auto step = [&](auto par, int ss) {  // ss + 1 < nss
+        constexpr int P = decltype(par)::value;  // == ss & 1
+        if constexpr (ADX == 2) {
+          load_a(std::integral_constant<int, P>{}, ss + 2 < nss ? ss + 2 : nss - 1);
+          load_b(bq[P ^ 1], ss + 1);
+          compute(bq[P], P);
+          store_a(P ^ 1, std::integral_constant<int, P ^ 1>{});
+        } else {
+          load_a(S0{}, ss + 1);
+          load_b(bq[P ^ 1], ss + 1);
+          compute(bq[P], P);
+          store_a(P ^ 1, S0{});
+        }
+        __syncthreads();
+      };
+      int ss = 0;
+      for (; ss + 2 < nss; ss += 2) {
+        step(std::integral_constant<int, 0>{}, ss);
+        step(std::integral_constant<int, 1>{}, ss + 1);
       }
-    };
-
-    // ---- pipeline: B one super-stage ahead in registers, A AD stages ahead
-    // in registers and double-buffered in LDS.  The last stage is peeled so
-    // that every prefetch in the loop is unconditional: a load behind a
-    // branch would make the wait before the next MFMA cover the loads just
-    // issued.  With AD = 2 what is stored after a stage's math was loaded
-    // before that stage's weights, so the store never waits on a load issued
-    // in the same stage (prefetches past the last stage re-read it).
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, AD - 1>;
-    load_a(S0{}, 0);
-    if constexpr (AD == 2) load_a(S1{}, nss > 1 ? 1 : 0);
-    load_b(bq[0], 0);
-    store_a(0, S0{});
-    __syncthreads();
-    auto step = [&](auto par, int ss) {  // ss + 1 < nss
-      constexpr int P = decltype(par)::value;  // == ss & 1
-      if constexpr (AD == 2) {
-        load_a(std::integral_constant<int, P>{}, ss + 2 < nss ? ss + 2 : nss - 1);
-        load_b(bq[P ^ 1], ss + 1);
-        compute(bq[P], P);
-        store_a(P ^ 1, std::integral_constant<int, P ^ 1>{});
+      if (ss + 1 < nss) {
+        step(std::integral_constant<int, 0>{}, ss);
+        compute(bq[1], 1);
       } else {
-        load_a(S0{}, ss + 1);
-        load_b(bq[P ^ 1], ss + 1);
-        compute(bq[P], P);
-        store_a(P ^ 1, S0{});
+        compute(bq[0], 0);
       }
       __syncthreads();
-    };
-    int ss = 0;
-    for (; ss + 2 < nss; ss += 2) {
-      step(std::integral_constant<int, 0>{}, ss);
-      step(std::integral_constant<int, 1>{}, ss + 1);
-    }
-    if (ss + 1 < nss) {
-      step(std::integral_constant<int, 0>{}, ss);
-      compute(bq[1], 1);
-    } else {
-      compute(bq[0], 0);
-    }
-    __syncthreads();
 
-    // ---- epilogue (A buffers are free: every wave passed the barrier above)
-    if constexpr (SWIGLU && C::FP8) {
-      // W8A8: z = silu(g) * u in fp32, staged in LDS
-      float *o32 = reinterpret_cast<float *>(lds);
-#pragma unroll
-      for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = b * 16 + q * 4 + i;
-          o32[row * BN + wave * 16 + r16] = silu_mul(acc[0][b][i], acc[1][b][i]);
-        }
-      __syncthreads();
-      if constexpr (BN == 128) {
-        // the item is exactly one 1x128 quantisation group wide: four
-        // threads per row take 32 columns each, share the row's amax and
-        // write E4M3 codes and the group scale (same arithmetic as the
-        // standalone quantiser)
-        constexpr int TPR = C::kThreads / BM;  // threads per row
-        static_assert(TPR * 32 == BN && TPR <= 64 && (64 % TPR) == 0, "row split");
-        for (int row = tid / TPR; row < BM; row += C::kThreads / TPR) {
-          const int part = tid % TPR;
-          const float *src = o32 + row * BN + part * 32;
-          float f[32];
-#pragma unroll
-          for (int c4 = 0; c4 < 8; ++c4) {
-            const u32x4 v = ld16(src + c4 * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) f[c4 * 4 + i] = __uint_as_float(v[i]);
+      // ---- epilogue (A buffers are free: every wave passed the barrier above)
+      if constexpr (SWIGLU && C::FP8) {
+        // W8A8: z = silu(g) * u in fp32, staged in LDS
+        float *o32 = reinterpret_cast<float *>(lds);
+  #pragma unroll
+        for (int b = 0; b < MB; ++b)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = b * 16 + q * 4 + i;
+            o32[row * BN + wave * 16 + r16] = silu_mul(acc[0][b][i], acc[1][b][i]);
           }
-          float amax = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-          for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-          const float sc = e4m3_scale(amax);
-          if (row < rows) {
-            uint8_t *dst = p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 + part * 32;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              uint32_t w[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                uint32_t word = 0;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb)
-                  word |= f32_to_e4m3(f[h2 * 16 + j * 4 + bb] / sc) << (8 * bb);
-                w[j] = word;
-              }
-              st16(dst + h2 * 16, u32x4{w[0], w[1], w[2], w[3]});
+        __syncthreads();
+        if constexpr (BN == 128) {
+          // the item is exactly one 1x128 quantisation group wide: four
+          // threads per row take 32 columns each, share the row's amax and
+          // write E4M3 codes and the group scale (same arithmetic as the
+          // standalone quantiser)
+          constexpr int TPR = C::kThreads / BM;  // threads per row
+          static_assert(TPR * 32 == BN && TPR <= 64 && (64 % TPR) == 0, "row split");
+          for (int row = tid / TPR; row < BM; row += C::kThreads / TPR) {
+            const int part = tid % TPR;
+            const float *src = o32 + row * BN + part * 32;
+            float f[32];
+  #pragma unroll
+            for (int c4 = 0; c4 < 8; ++c4) {
+              const u32x4 v = ld16(src + c4 * 4);
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) f[c4 * 4 + i] = __uint_as_float(v[i]);
             }
-            if (part == 0)
-              p.c_scale[static_cast<int64_t>(tile.row0 + row) * p.c_scale_pitch + n0 / 128] = sc;
+            float amax = 0.0f;
+  #pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  #pragma unroll
+            for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const float sc = e4m3_scale(amax);
+            if (row < rows) {
+              uint8_t *dst = p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 + part * 32;
+  #pragma unroll
+              for (int h2 = 0; h2 < 2; ++h2) {
+                uint32_t w[4];
+  #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  uint32_t word = 0;
+  #pragma unroll
+                  for (int bb = 0; bb < 4; ++bb)
+                    word |= f32_to_e4m3(f[h2 * 16 + j * 4 + bb] / sc) << (8 * bb);
+                  w[j] = word;
+                }
+                st16(dst + h2 * 16, u32x4{w[0], w[1], w[2], w[3]});
+              }
+              if (part == 0)
+                p.c_scale[static_cast<int64_t>(tile.row0 + row) * p.c_scale_pitch + n0 / 128] = sc;
+            }
+          }
+        } else {
+          // a quantisation group spans two items: z stays fp32 and the 1x128
+          // quantiser runs on it afterwards
+          constexpr int PIECES = BM * BN * 4 / 16;
+          for (int c = tid; c < PIECES; c += C::kThreads) {
+            const int row = c / (BN * 4 / 16), col = c % (BN * 4 / 16);
+            if (row < rows)
+              st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 4 + col * 16,
+                   ld16(lds + row * BN * 4 + col * 16));
           }
         }
       } else {
-        // a quantisation group spans two items: z stays fp32 and the 1x128
-        // quantiser runs on it afterwards
-        constexpr int PIECES = BM * BN * 4 / 16;
+        uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
+  #pragma unroll
+        for (int b = 0; b < MB; ++b)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = b * 16 + q * 4 + i;
+            const float v = SWIGLU ? silu_mul(acc[0][b][i], acc[NMAT - 1][b][i]) : acc[0][b][i];
+            o16[row * BN + wave * 16 + r16] = f32_to_bf16(v);
+          }
+        __syncthreads();
+        constexpr int PIECES = BM * BN * 2 / 16;
         for (int c = tid; c < PIECES; c += C::kThreads) {
-          const int row = c / (BN * 4 / 16), col = c % (BN * 4 / 16);
+          const int row = c / (BN * 2 / 16), col = c % (BN * 2 / 16);
           if (row < rows)
-            st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 4 + col * 16,
-                 ld16(lds + row * BN * 4 + col * 16));
+            st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
+                 ld16(lds + row * BN * 2 + col * 16));
         }
       }
-    } else {
-      uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
-#pragma unroll
-      for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = b * 16 + q * 4 + i;
-          const float v = SWIGLU ? silu_mul(acc[0][b][i], acc[NMAT - 1][b][i]) : acc[0][b][i];
-          o16[row * BN + wave * 16 + r16] = f32_to_bf16(v);
-        }
-      __syncthreads();
-      constexpr int PIECES = BM * BN * 2 / 16;
-      for (int c = tid; c < PIECES; c += C::kThreads) {
-        const int row = c / (BN * 2 / 16), col = c % (BN * 2 / 16);
-        if (row < rows)
-          st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
-               ld16(lds + row * BN * 2 + col * 16));
-      }
-    }
+    };
+    const int passes = (rows + RPP - 1) / RPP;
+    using Full = std::integral_constant<int, RA>;
+    using Half = std::integral_constant<int, (RA % 2 == 0 ? RA / 2 : RA)>;
+    using Quarter = std::integral_constant<int, (RA % 4 == 0 ? RA / 4 : RA)>;
+    using Two = std::integral_constant<int, 2>;
+    // Only the bf16 128-row shapes take the shorter paths: in fp8 three
+    // copies of the body do not fit the register budget together, and the
+    // 64-row gate/up shape spills more and ran slower with them.
+    constexpr bool kPaths = !C::FP8 && BM == 128;
+    if (kPaths && RA % 4 == 0 && passes <= RA / 4)
+      body(Quarter{}, Two{});
+    else if (kPaths && RA % 2 == 0 && passes <= RA / 2)
+      body(Half{}, Two{});
+    else
+      body(Full{}, std::integral_constant<int, AD>{});
     // the next item's first barrier orders these LDS reads before reuse
   }
 }
