@@ -20,7 +20,9 @@
 //    GEMMs load them (and in fp8 the scales the store needs) two
 //    super-stages ahead, so that storing them to LDS never waits on a load
 //    issued in the same stage; the gate/up shapes load them one stage ahead
-//    (two spill registers in bf16 and are slower in fp8).
+//    (two spill registers in bf16 and are slower in fp8).  The bf16 128-row
+//    shapes stage only the passes a tile's rows fill and, when that is half
+//    or a quarter of them, load two stages ahead with the registers saved.
 //  * bf16: chunk i is one 16x16x32 MFMA.  fp8: chunks 2b and 2b+1 (bytes
 //    [128 b + 16 q] and [128 b + 64 + 16 q]) lie in the same 128-wide K
 //    block b and feed one 16x16x128 MFMA; the block's partial sum is then
