@@ -13,14 +13,14 @@
 // the same columns.
 //
 // Operands move with direct-to-LDS loads (global_load_lds, no staging
-// registers) into a ring of five 32 KB half-stage slots (all 160 KB of LDS):
-// half-stage 2s holds the weight rows of stage s, 2s + 1 its activation
-// rows.  While the MFMAs read stage s, the activation rows of stage s + 1
-// and the weight rows of stage s + 2 load, issued one at a time between the
-// first K steps' MFMAs: weights (from HBM) get two stages to arrive,
-// activations (shared by the column tiles of a row tile, mostly L2 hits)
-// one.  Ordering uses an explicit vmcnt wait plus a bare s_barrier per
-// stage (a full workgroup fence would drain every outstanding load).  LDS rows are 128 bytes with the 16-byte chunk index XOR-ed by
+// registers) into two 64 KB stage buffers: the next stage loads while the
+// MFMAs read the current one, its loads issued one at a time between the
+// first K steps' MFMAs.  Ordering uses an explicit vmcnt(0) wait plus a
+// bare s_barrier per stage (a full workgroup fence would drain every
+// outstanding load).  The wait is for zero on purpose: with several stages
+// of direct-to-LDS loads in flight, a wait that leaves the newest loads
+// outstanding did not guarantee that the older ones had landed in LDS (a
+// deeper ring built that way gave run-to-run different results).  LDS rows are 128 bytes with the 16-byte chunk index XOR-ed by
 // (row / 2) % 8, so the 16 rows one MFMA operand read touches per quarter
 // wave hit 16 different 4-bank groups.  (32-element stages in a deeper ring
 // fetched half lines and ran 7-9% slower.)
@@ -41,9 +41,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kBM = 256;    // rows per tile
 constexpr int kBW = 256;    // weight rows per tile
 constexpr int kStage = 128;  // bytes per row per K stage (64 bf16)
-constexpr int kHalf = kBM * kStage;  // one operand of one stage: 32 KB
-constexpr int kSlots = 5;            // half-stage ring: 160 KB
-static_assert(kBM == kBW, "both operands of a stage fill one half-stage slot");
+constexpr int kRing = 2;    // LDS double buffer
+constexpr int kSlot = (kBM + kBW) * kStage;  // 64 KB
 
 // byte offset of 16-byte chunk `chunk` (0..7) of LDS row `row`: the chunk
 // index is XOR-ed with (row / 2) % 8 (see the file comment)
@@ -65,7 +64,8 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_dst) {
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
-  extern __shared__ __align__(16) uint8_t lds[];  // kSlots x 32 KB
+  extern __shared__ __align__(16) uint8_t lds[];  // kRing x (A 32 KB + B 32 KB)
+  __shared__ int rowsrc[kBM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 2, wc = wave & 3;   // 2 x 4 waves: 128 rows x 64 weight rows each
@@ -88,12 +88,15 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   const int gi = shared ? tile.group - p.E : tile.group;
   const int rows = tile.rows;
 
-  // source row of activation row `row` of the tile; rows past the tile's
-  // end read its first row
-  auto source_row = [&](int row) {
-    const int r = tile.row0 + (row < rows ? row : 0);
-    return p.perm ? (r < p.Tk ? p.perm[r] : (r - p.Tk) % p.T) : r;
-  };
+  if (tid < kBM) {
+    int src = -1;
+    if (tid < rows) {
+      const int r = tile.row0 + tid;
+      src = p.perm ? (r < p.Tk ? p.perm[r] : (r - p.Tk) % p.T) : r;
+    }
+    rowsrc[tid] = src;
+  }
+  __syncthreads();
 
   const int64_t krow = static_cast<int64_t>(K) * 2;
   const int nst = static_cast<int>(krow / kStage);
@@ -101,32 +104,34 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   const uint8_t *B0 = (shared ? p.sb0 : p.b0) + gi * mat;
   const uint8_t *B1 = SWIGLU ? (shared ? p.sb1 : p.b1) + gi * mat : B0;
 
-  // Each wave moves rows [32 wave, 32 wave + 32) of the A half-stage and of
-  // the B half-stage: four 1 KB direct-to-LDS loads each (8 rows of 128
-  // bytes per load).  Lane i fills LDS row 8 h + i / 8, position i % 8,
-  // which holds the row's 16-byte chunk (i % 8) ^ ((row / 2) % 8) (bank
-  // swizzle).  Rows past the tile's end load a valid row (rows of an MFMA
-  // tile are independent; those results are never stored); weight rows past
-  // N (a partial last column tile) load row N - 1.
+  // Each wave moves rows [32 wave, 32 wave + 32) of the A stage and of the
+  // B stage: four 1 KB direct-to-LDS loads each (8 rows of 128 bytes per
+  // load).  Lane i fills LDS row 8 h + i / 8, position i % 8, which holds
+  // the row's 16-byte chunk (i % 8) ^ ((row / 2) % 8) (bank swizzle).
+  // Rows past the tile's end load a valid row (rows of an MFMA tile are
+  // independent; those results are never stored); weight rows past N (a
+  // partial last column tile) load row N - 1.
+  const int src_first = rowsrc[0];
   const uint8_t *asrc[4];
   const uint8_t *bsrc[4];
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
     const int row = wave * 32 + hh * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);
-    asrc[hh] = p.A + static_cast<int64_t>(source_row(row)) * p.a_pitch + ch * 16;
+    const int src = rowsrc[row] >= 0 ? rowsrc[row] : src_first;
+    asrc[hh] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
     const int n = n0 + (SWIGLU ? (row & (kBW / 2 - 1)) : row);
     const uint8_t *base = (SWIGLU && row >= kBW / 2) ? B1 : B0;
     bsrc[hh] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16;
   }
-  // half-stage h lives in slot h % kSlots; B of stage s is h = 2 s, A is
-  // h = 2 s + 1
-  auto slot_of = [&](int h) { return lds + (h % kSlots) * kHalf + wave * 4 * 1024; };
-  auto issue_a = [&](int s, int hh) {
-    dma16(asrc[hh] + static_cast<int64_t>(s) * kStage, slot_of(2 * s + 1) + hh * 1024);
-  };
-  auto issue_b = [&](int s, int hh) {
-    dma16(bsrc[hh] + static_cast<int64_t>(s) * kStage, slot_of(2 * s) + hh * 1024);
+  auto issue = [&](int s) {  // stage s -> ring slot s % kRing
+    uint8_t *slot = lds + (s % kRing) * kSlot;
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      dma16(asrc[hh] + static_cast<int64_t>(s) * kStage, slot + (wave * 4 + hh) * 1024);
+      dma16(bsrc[hh] + static_cast<int64_t>(s) * kStage,
+            slot + kBM * kStage + (wave * 4 + hh) * 1024);
+    }
   };
 
   f32x16 acc[4][2];
@@ -140,30 +145,19 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   const int wrow0 = SWIGLU ? wc * 32 + r32 : wc * 64 + r32;
   const int wrow1 = SWIGLU ? kBW / 2 + wc * 32 + r32 : wc * 64 + 32 + r32;
 
-  // prologue: B and A of stage 0, B of stage 1 (issue order B0, A0, B1;
-  // stage s then issues A of s + 1 and B of s + 2, in that order)
+  // prologue: stage 0 in flight
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh) issue_b(0, hh);
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) issue_a(0, hh);
-  if (nst > 1)
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) issue_b(1, hh);
+  for (int s = 0; s < kRing - 1; ++s)
+    if (s < nst) issue(s);
   for (int s = 0; s < nst; ++s) {
-    // vector loads complete in order: everything up to A of stage s is
-    // done once at most this wave's four loads of B of stage s + 1 (the last
-    // issued) are outstanding
-    if (s + 1 < nst)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // after the barrier every wave is done with stage s - 1, whose slots
-    // (half-stages 2 s - 2 and 2 s - 1) take A of s + 1 and B of s + 2
+    // double buffer: only stage s is in flight here
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    const bool issue_next_a = s + 1 < nst;
-    const bool issue_next_b = s + 2 < nst;
-    const uint8_t *la = lds + ((2 * s + 1) % kSlots) * kHalf;
-    const uint8_t *lb = lds + ((2 * s) % kSlots) * kHalf;
+    const bool do_issue = s + 1 < nst;
+    const int si = s + 1;
+    uint8_t *slot = lds + (si % kRing) * kSlot;
+    const uint8_t *la = lds + (s % kRing) * kSlot;
+    const uint8_t *lb = la + kBM * kStage;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int ch = 2 * ks + g;
@@ -178,12 +172,19 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[m], fb[n], acc[m][n], 0, 0, 0);
-        if (ks == 0 && issue_next_a) issue_a(s + 1, m);
-        if (ks == 1 && issue_next_b) issue_b(s + 2, m);
+        if (ks < 2 && do_issue) {
+          const int idx = ks * 4 + m;  // 0..7
+          const int hh = idx >> 1;
+          if ((idx & 1) == 0)
+            dma16(asrc[hh] + static_cast<int64_t>(si) * kStage, slot + (wave * 4 + hh) * 1024);
+          else
+            dma16(bsrc[hh] + static_cast<int64_t>(si) * kStage,
+                  slot + kBM * kStage + (wave * 4 + hh) * 1024);
+        }
       }
     }
   }
-  __syncthreads();  // all waves are done with the ring (and no load is in flight)
+  __syncthreads();  // all waves are done with the ring before the epilogue reuses it
 
   // ---- epilogue: stage the bf16 tile in LDS, then whole 16-byte stores.
   // acc[m][n][i]: row 32 m + 8 (i / 4) + 4 g + (i % 4), column r32 of block n.
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
 template <bool SWIGLU>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
-  constexpr size_t kLds = kSlots * kHalf;  // 5 x 32 KB
+  constexpr size_t kLds = kRing * kSlot;  // 2 x 64 KB
   // the dynamic-LDS limit is a per-device attribute of the kernel
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> attr_set[kMaxDevices];
