@@ -172,6 +172,32 @@ def test_determinism_and_microbatch_split():
 
 
 @pytest.mark.parametrize("shape", [
+    LayerShape("rep_bf16_bm64", T=256, h=1024, E=64, k=8, I=512, S=1, Is=512, mode="bf16"),
+    LayerShape("rep_bf16_bm128", T=512, h=1024, E=64, k=8, I=512, S=1, Is=512, mode="bf16"),
+    LayerShape("rep_bf16_prefill", T=2048, h=1024, E=8, k=2, I=512, S=1, Is=512, mode="bf16"),
+    LayerShape("rep_w8a8_stream", T=512, h=1024, E=64, k=8, I=512, S=1, Is=512, mode="w8a8"),
+    LayerShape("rep_w8a8_tiled", T=2048, h=1024, E=8, k=2, I=512, S=1, Is=512, mode="w8a8"),
+    LayerShape("rep_f32", T=128, h=256, E=8, k=2, I=256, S=1, Is=256, mode="f32"),
+], ids=lambda s: s.name)
+def test_repeated_forwards_are_bitwise_identical(shape):
+    """Many forwards of one input give the same bits every time, for every
+    kernel family: a pipeline that read a buffer before all of its loads
+    had landed would show up here as run-to-run differences."""
+    syn = SyntheticLayer(shape, seed=21)
+    from expert_side_attention_amd.workload import build_layer, to_device
+    layer = build_layer(syn, DEV)
+    x = to_device(syn.hidden(), DEV, shape.mode != "f32")
+    ref = layer.forward(x).clone()
+    out = torch.empty_like(ref)
+    iv = torch.int32 if shape.mode == "f32" else torch.int16
+    for i in range(24):
+        layer.forward(x, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(iv), ref.view(iv)), f"forward {i}"
+    layer.close()
+
+
+@pytest.mark.parametrize("shape", [
     # decode-regime plans: every expert's rows sit in one tile of one kernel,
     # whose per-row arithmetic does not depend on the row's position
     LayerShape("perm_bf16_bm128", T=300, h=256, E=16, k=4, I=256, S=1, Is=128, mode="bf16"),
