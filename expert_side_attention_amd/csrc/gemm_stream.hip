@@ -470,10 +470,20 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
   auto fits = [&](int64_t ss) { return (a.K * es) % ss == 0 && (a.Ks * es) % ss == 0; };
   if (elem == 1) {
     if (bm == 64) {
-      if (gu)
+      if (gu) {
+        // With many items per resident workgroup (DeepSeek-V3 decode shapes)
+        // 8 waves x 128 columns stage each activation row half as often; with
+        // few (3 per workgroup on the decode h4096 layer) the 4-wave shape's
+        // smaller items finish closer together.
+        const int nmax = a.N > a.Ns ? a.N : a.Ns;
+        const int64_t items128 = static_cast<int64_t>(a.tiles_ub) * (nmax / 128);
+        if (fits(512) && items128 >= 2048)
+          return launch_stream<Elem::BF16, 8, 64, 512, true>(a, s);
         return fits(512) ? launch_stream<Elem::BF16, 4, 64, 512, true>(a, s)
                          : launch_stream<Elem::BF16, 4, 64, 128, true>(a, s);
-      return launch_stream<Elem::BF16, 8, 64, 256, false, 2>(a, s);
+      }
+      return fits(512) ? launch_stream<Elem::BF16, 8, 64, 512, false, 2>(a, s)
+                       : launch_stream<Elem::BF16, 8, 64, 256, false, 2>(a, s);
     }
     if (bm == 128) {
       if (gu)
