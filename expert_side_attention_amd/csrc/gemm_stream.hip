@@ -17,12 +17,13 @@
 //    whole 64-byte row segments.
 //  * The gathered activation rows (a few KB per tile, shared by all waves)
 //    are staged through LDS, double-buffered per super-stage.  The down
-//    GEMMs load them (and in fp8 the scales the store needs) two
-//    super-stages ahead, so that storing them to LDS never waits on a load
-//    issued in the same stage; the gate/up shapes load them one stage ahead
-//    (two spill registers in bf16 and are slower in fp8).  The bf16 128-row
-//    shapes stage only the passes a tile's rows fill and, when that is half
-//    or a quarter of them, load two stages ahead with the registers saved.
+//    GEMMs and the 128-row fp8 gate/up GEMM load them (and in fp8 the
+//    scales the store needs) two super-stages ahead, so that storing them
+//    to LDS never waits on a load issued in the same stage; the bf16
+//    gate/up shapes load them one stage ahead (the second slot spills
+//    there).  The bf16 128-row shapes stage only the passes a tile's rows
+//    fill and, when that is half or a quarter of them, load two stages
+//    ahead with the registers saved.
 //  * bf16: chunk i is one 16x16x32 MFMA.  fp8: chunks 2b and 2b+1 (bytes
 //    [128 b + 16 q] and [128 b + 64 + 16 q]) lie in the same 128-wide K
 //    block b and feed one 16x16x128 MFMA; the block's partial sum is then
@@ -501,7 +502,7 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
     }
     if (bm == 128)
       // both gate/up shapes are 128 columns wide: stream_gate_up_writes_fp8
-      return gu ? (fits(256) ? launch_stream<Elem::FP8, 8, 128, 256, true>(a, s)
+      return gu ? (fits(256) ? launch_stream<Elem::FP8, 8, 128, 256, true, 2>(a, s)
                           : launch_stream<Elem::FP8, 8, 128, 128, true>(a, s))
                 : launch_stream<Elem::FP8, 8, 128, 128, false, 2>(a, s);
   }
