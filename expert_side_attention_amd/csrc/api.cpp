@@ -205,7 +205,9 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
       {reinterpret_cast<void **>(&h->counters), 2 * sizeof(int32_t)},
       {reinterpret_cast<void **>(&h->dispatch_scratch),
        sizeof(int32_t) * 2 * afd::dispatch_blocks(static_cast<int>(T)) * E},
-      {reinterpret_cast<void **>(&h->logits), sizeof(float) * T * E},
+      {reinterpret_cast<void **>(&h->logits),
+       sizeof(float) * static_cast<size_t>(afd::router_logit_floats(
+                           static_cast<int>(T), cfg->hidden, static_cast<int>(E)))},
       {reinterpret_cast<void **>(&h->tiles), sizeof(afd::Tile) * h->tiles_cap},
       {reinterpret_cast<void **>(&h->tiles_big), sizeof(afd::Tile) * h->big_cap},
       {reinterpret_cast<void **>(&h->z), static_cast<size_t>(R) * h->zpitch * zes},

@@ -62,8 +62,16 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_dst) {
                                    (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
 
-template <bool SWIGLU>
+// MODE: kDown (C = A B0^T, bf16), kGateUp (C = silu(A B0^T) * (A B1^T),
+// bf16), kLogits (router logits: A = X rows, B0 = router weight, no tile
+// list; blockIdx.y picks one of gridDim.y equal K ranges and the fp32
+// partial sums go to plane blockIdx.y of C, planes c_plane floats apart).
+enum { kDown = 0, kGateUp = 1, kLogits = 2 };
+
+template <int MODE>
 __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
+  constexpr bool SWIGLU = MODE == kGateUp;
+  constexpr bool LOGITS = MODE == kLogits;
   extern __shared__ __align__(16) uint8_t lds[];  // kRing x (A 32 KB + B 32 KB)
   __shared__ int rowsrc[kBM];
 
@@ -78,8 +86,14 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   const int j = L >> 3;
   const int mt = (L & 7) + 8 * (j / ntn);
   const int nt = j % ntn;
-  if (mt >= *p.num_tiles) return;
-  const Tile tile = p.tiles[mt];
+  Tile tile;
+  if constexpr (LOGITS) {
+    if (mt * kBM >= p.T) return;
+    tile = Tile{0, mt * kBM, min(kBM, p.T - mt * kBM), 0};
+  } else {
+    if (mt >= *p.num_tiles) return;
+    tile = p.tiles[mt];
+  }
   const bool shared = tile.group >= p.E;
   const int N = shared ? p.Ns : p.N;
   const int K = shared ? p.Ks : p.K;
@@ -99,7 +113,10 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   __syncthreads();
 
   const int64_t krow = static_cast<int64_t>(K) * 2;
-  const int nst = static_cast<int>(krow / kStage);
+  // this workgroup's stages [s_begin, s_begin + nst) of the K range
+  const int nst_all = static_cast<int>(krow / kStage);
+  const int s_begin = static_cast<int>(static_cast<int64_t>(blockIdx.y) * nst_all / gridDim.y);
+  const int nst = static_cast<int>(static_cast<int64_t>(blockIdx.y + 1) * nst_all / gridDim.y) - s_begin;
   const int64_t mat = static_cast<int64_t>(N) * krow;
   const uint8_t *B0 = (shared ? p.sb0 : p.b0) + gi * mat;
   const uint8_t *B1 = SWIGLU ? (shared ? p.sb1 : p.b1) + gi * mat : B0;
@@ -119,10 +136,12 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
     const int row = wave * 32 + hh * 8 + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);
     const int src = rowsrc[row] >= 0 ? rowsrc[row] : src_first;
-    asrc[hh] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
+    asrc[hh] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16 +
+               static_cast<int64_t>(s_begin) * kStage;
     const int n = n0 + (SWIGLU ? (row & (kBW / 2 - 1)) : row);
     const uint8_t *base = (SWIGLU && row >= kBW / 2) ? B1 : B0;
-    bsrc[hh] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16;
+    bsrc[hh] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16 +
+               static_cast<int64_t>(s_begin) * kStage;
   }
   auto issue = [&](int s) {  // stage s -> ring slot s % kRing
     uint8_t *slot = lds + (s % kRing) * kSlot;
@@ -186,6 +205,25 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   }
   __syncthreads();  // all waves are done with the ring before the epilogue reuses it
 
+  if constexpr (LOGITS) {
+    // fp32 partial logits straight from the accumulators: for each register,
+    // the 32 lanes of a half-wave write 32 consecutive experts of one token
+    float *plane = reinterpret_cast<float *>(p.C) + static_cast<int64_t>(blockIdx.y) * p.c_plane;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = wr * 128 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int col = n0 + wc * 64 + n * 32 + r32;
+          if (row < rows && col < N)
+            plane[static_cast<int64_t>(tile.row0 + row) * N + col] = acc[m][n][i];
+        }
+      }
+    return;
+  }
+
   // ---- epilogue: stage the bf16 tile in LDS, then whole 16-byte stores.
   // acc[m][n][i]: row 32 m + 8 (i / 4) + 4 g + (i % 4), column r32 of block n.
   uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
@@ -215,9 +253,8 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   }
 }
 
-template <bool SWIGLU>
-hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
-  constexpr int BNO = SWIGLU ? kBW / 2 : kBW;
+template <int MODE>
+hipError_t set_lds_limit() {
   constexpr size_t kLds = kRing * kSlot;  // 2 x 64 KB
   // the dynamic-LDS limit is a per-device attribute of the kernel
   constexpr int kMaxDevices = 64;
@@ -227,23 +264,63 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   if (!attr_set[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_gemm_kernel<SWIGLU>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_gemm_kernel<MODE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
   }
+  return hipSuccess;
+}
+
+template <int MODE>
+hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
+  constexpr int BNO = MODE == kGateUp ? kBW / 2 : kBW;
+  hipError_t e = set_lds_limit<MODE>();
+  if (e != hipSuccess) return e;
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int ntn = (nmax + BNO - 1) / BNO;
   const int64_t grid = 8LL * ((a.tiles_ub + 7) / 8) * ntn;
   if (grid <= 0) return hipSuccess;
-  prefill_gemm_kernel<SWIGLU><<<static_cast<unsigned>(grid), 512, kLds, s>>>(a);
+  prefill_gemm_kernel<MODE><<<static_cast<unsigned>(grid), 512, kRing * kSlot, s>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_prefill(GemmKind kind, const GemmArgs &a, hipStream_t s) {
-  return kind == GemmKind::GateUp ? launch_one<true>(a, s) : launch_one<false>(a, s);
+  return kind == GemmKind::GateUp ? launch_one<kGateUp>(a, s) : launch_one<kDown>(a, s);
+}
+
+int logits_splits(int T, int h, int E) {
+  const int rtiles = (T + kBM - 1) / kBM, ctiles = (E + kBW - 1) / kBW;
+  const int nst = h * 2 / kStage;
+  int ks = 256 / (rtiles * ctiles);  // about one workgroup per CU
+  if (ks > nst / 7) ks = nst / 7;    // at least 7 stages per split
+  if (ks > 16) ks = 16;
+  return ks < 1 ? 1 : ks;
+}
+
+hipError_t launch_logits_gemm(const uint16_t *x, const uint16_t *wr, int T, int h, int E,
+                              float *partials, int splits, hipStream_t s) {
+  hipError_t e = set_lds_limit<kLogits>();
+  if (e != hipSuccess) return e;
+  GemmArgs a{};
+  a.A = reinterpret_cast<const uint8_t *>(x);
+  a.a_pitch = static_cast<int64_t>(h) * 2;
+  a.perm = nullptr;
+  a.T = T;
+  a.Tk = T;
+  a.b0 = reinterpret_cast<const uint8_t *>(wr);
+  a.N = a.Ns = E;
+  a.K = a.Ks = h;
+  a.E = 1;
+  a.C = reinterpret_cast<uint8_t *>(partials);
+  a.c_plane = static_cast<int64_t>(T) * E;
+  const int rtiles = (T + kBM - 1) / kBM, ctiles = (E + kBW - 1) / kBW;
+  const dim3 grid(static_cast<unsigned>(8 * ((rtiles + 7) / 8) * ctiles),
+                  static_cast<unsigned>(splits));
+  prefill_gemm_kernel<kLogits><<<grid, 512, kRing * kSlot, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace afd

@@ -21,7 +21,8 @@ constexpr int kMaxShared = 8;
 
 // Router GEMM + softmax + top-k + renormalisation.
 // f32: x, wr are fp32; else bf16.  bias may be null.  bf16 path scratch:
-// logits [T, E] fp32.
+// logits, router_logit_floats(T, h, E) floats.
+int64_t router_logit_floats(int T, int h, int E);
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
                          float *logits, int32_t *ids, float *w, hipStream_t s);
@@ -84,6 +85,7 @@ struct GemmArgs {
   int64_t c_pitch;
   float *c_scale;        // fp8 GateUp: [R, c_scale_pitch]
   int c_scale_pitch;
+  int64_t c_plane;       // router logits GEMM: floats between split-K planes
 };
 
 // GEMM plan of a forward: the tile lists and the kernel family that runs
@@ -106,6 +108,12 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
                               hipStream_t s);
 // Compute-bound kernel (bf16, bm 256).
 hipError_t launch_gemm_prefill(GemmKind kind, const GemmArgs &a, hipStream_t s);
+// Router logits of long batches on the compute-bound kernel: partials[p][t][e]
+// = sum over the p-th of `splits` equal K ranges of x[t] . wr[e] (fp32);
+// logits_splits picks `splits` for a shape.
+int logits_splits(int T, int h, int E);
+hipError_t launch_logits_gemm(const uint16_t *x, const uint16_t *wr, int T, int h, int E,
+                              float *partials, int splits, hipStream_t s);
 
 // out[t] = sum_j w[t,j] Y[slot_row[t,j]] + sum_s Y[Tk + s*T + t].
 hipError_t launch_combine(bool f32, const uint8_t *Y, const int32_t *slot_row,

@@ -16,6 +16,11 @@
 namespace afd {
 namespace {
 
+// bf16 batches above this many tokens take the LDS-tiled logits GEMM (at
+// 8192 tokens of DeepSeek-V3 width it takes the router from 153 to 90 us; at
+// 2048 the register-operand kernel below is faster, 55 against 76 us)
+constexpr int kTiledRouterT = 4096;
+
 // Sortable key: larger logit first, then smaller index.  Key 0 = removed.
 __device__ __forceinline__ unsigned long long topk_key(float v, int e) {
   v += 0.0f;  // -0 -> +0 so equal logits compare equal
@@ -38,21 +43,30 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
 
 // Top-k over the logits of TM tokens (row pitch E, in LDS or global memory),
 // one wave per token at a time.  NC = candidates per lane (E <= 64 * NC).
+// A logit is the sum of `planes` partial values `plane` floats apart, added
+// in plane order, plus bias[e] when bias is not null.
 template <int TM, int NC, int WAVES = 4>
 __device__ void topk_rows(const float *sl, float *selv, int t0, int T,
-                          int E, int k, int32_t *ids, float *wout) {
+                          int E, int k, int32_t *ids, float *wout, int planes = 1,
+                          int64_t plane = 0, const float *bias = nullptr) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   float *mysel = selv + wave * kMaxExperts;
   for (int tt = wave; tt < TM; tt += WAVES) {
     const int t = t0 + tt;
     if (t >= T) break;
-    const float *row = sl + tt * E;
+    const float *row = sl + static_cast<int64_t>(tt) * E;
+    auto logit = [&](int e) {
+      float v = row[e];
+      for (int pl = 1; pl < planes; ++pl) v += row[pl * plane + e];
+      if (bias) v += bias[e];
+      return v;
+    };
     unsigned long long key[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = lane + 64 * c;
-      key[c] = e < E ? topk_key(row[e], e) : 0ull;
+      key[c] = e < E ? topk_key(logit(e), e) : 0ull;
     }
     for (int j = 0; j < k; ++j) {
       unsigned long long best = 0;
@@ -65,7 +79,7 @@ __device__ void topk_rows(const float *sl, float *selv, int t0, int T,
         if (lane + 64 * c == e) key[c] = 0;
       if (lane == 0) {
         ids[static_cast<int64_t>(t) * k + j] = e;
-        mysel[j] = row[e];
+        mysel[j] = logit(e);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -176,14 +190,17 @@ __global__ __launch_bounds__(WAVES * 64) void router_bf16_kernel(
   }
 }
 
-// Top-k and weights from the logits: one wave per token, four per workgroup.
+// Top-k and weights from the logits (the sum of `planes` partial planes plus
+// bias, if given): one wave per token, four per workgroup.
 template <int NC>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T,
                                                    int E, int k, int32_t *__restrict__ ids,
-                                                   float *__restrict__ wout) {
+                                                   float *__restrict__ wout, int planes,
+                                                   const float *__restrict__ bias) {
   __shared__ float selv[4 * kMaxExperts];
   const int t0 = blockIdx.x * 4;
-  topk_rows<4, NC, 4>(logits + static_cast<int64_t>(t0) * E, selv, t0, T, E, k, ids, wout);
+  topk_rows<4, NC, 4>(logits + static_cast<int64_t>(t0) * E, selv, t0, T, E, k, ids, wout,
+                      planes, static_cast<int64_t>(T) * E, bias);
 }
 
 // fp32 router for small layers: one (token, expert) dot product per thread.
@@ -225,10 +242,24 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   }
   const uint16_t *X = static_cast<const uint16_t *>(x);
   const uint16_t *W = static_cast<const uint16_t *>(wr);
-  // token blocks of 16 (32 up to 4096 tokens, 64 above), expert slices sized
-  // so that a batch launches a few hundred workgroups, K split over 8 waves
-  // (4 for the 64-token blocks, whose partial sums would not fit LDS
-  // otherwise)
+  const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
+  auto topk = [&](int planes, const float *b) {
+    if (E <= 64) topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b);
+    else if (E <= 256) topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b);
+    else topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b);
+    return hipGetLastError();
+  };
+  if (T > kTiledRouterT) {
+    // long batches: LDS-tiled 256 x 256 GEMM with the K range split over
+    // workgroups; the top-k adds the partial planes in order, then the bias
+    const int splits = logits_splits(T, h, E);
+    hipError_t e = launch_logits_gemm(X, W, T, h, E, logits, splits, s);
+    if (e != hipSuccess) return e;
+    return topk(splits, bias);
+  }
+  // token blocks of 16 (32 above 1024 tokens), expert slices sized so that
+  // a batch launches a few hundred workgroups, K split over 8 waves (4 when
+  // h is not a multiple of 256)
 #define AFD_ROUTER(TM, EN, NBUF, WAVES)                                                 \
   router_bf16_kernel<TM, EN, NBUF, WAVES>                                              \
       <<<dim3((E + EN - 1) / EN, (T + TM - 1) / TM), WAVES * 64, 0, s>>>(X, W, bias, T, h, \
@@ -239,8 +270,6 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   if (E > 256) {
     if (k8) AFD_ROUTER(16, 64, 4, 8);
     else AFD_ROUTER(16, 64, 4, 4);
-  } else if (T > 4096) {
-    AFD_ROUTER(64, 64, 4, 4);
   } else if (T > 1024) {
     if (k8) AFD_ROUTER(32, 64, 4, 8);
     else AFD_ROUTER(32, 64, 4, 4);
@@ -254,11 +283,17 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
 #undef AFD_ROUTER
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
-  if (E <= 64) topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w);
-  else if (E <= 256) topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w);
-  else topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w);
-  return hipGetLastError();
+  return topk(1, nullptr);
+}
+
+int64_t router_logit_floats(int T, int h, int E) {
+  (void)h;
+  if (T <= kTiledRouterT) return static_cast<int64_t>(T) * E;
+  // tiled path, t tokens: splits <= 16, and either splits = 1 or
+  // splits x row tiles <= 256 with t <= 256 x row tiles, so the planes hold
+  // splits x t <= max(t, min(16 t, 65536)) rows
+  const int64_t rows16 = 16LL * T < 65536 ? 16LL * T : 65536;
+  return (T > rows16 ? T : rows16) * static_cast<int64_t>(E);
 }
 
 }  // namespace afd

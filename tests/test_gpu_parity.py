@@ -91,6 +91,9 @@ SMALL = [
 LONG = [
     LayerShape("bf16_t65536", T=65536, h=128, E=64, k=8, I=128, S=1, Is=128, mode="bf16"),
     LayerShape("w8a8_t32768", T=32768, h=256, E=32, k=2, I=128, S=1, Is=128, mode="w8a8"),
+    # the tiled router: K split in two, a partial second column tile of experts
+    LayerShape("bf16_router_tiled", T=4500, h=1024, E=320, k=4, I=128, S=1, Is=128,
+               mode="bf16"),
 ]
 
 
