@@ -28,6 +28,11 @@
 // Tile order: row tiles are dealt round-robin to the 8 XCDs (workgroup ids
 // go to XCDs round-robin) and all column tiles of a row tile run on one XCD,
 // close in time: the XCD's L2 serves the activation rows to all of them.
+//
+// The same kernel also computes router logits of long batches (logits
+// mode): rows of X against the router weight, the K range split over
+// workgroups, fp32 partial sums written straight from the accumulators to
+// one plane per split (the top-k kernel adds the planes).
 #include "common.h"
 #include <atomic>
 
@@ -296,7 +301,7 @@ int logits_splits(int T, int h, int E) {
   const int nst = h * 2 / kStage;
   int ks = 256 / (rtiles * ctiles);  // about one workgroup per CU
   if (ks > nst / 7) ks = nst / 7;    // at least 7 stages per split
-  if (ks > 16) ks = 16;
+  if (ks > kMaxLogitSplits) ks = kMaxLogitSplits;
   return ks < 1 ? 1 : ks;
 }
 

@@ -17,6 +17,7 @@ struct Tile {
 };
 
 constexpr int kMaxExperts = 512;
+constexpr int kMaxLogitSplits = 16;
 constexpr int kMaxShared = 8;
 
 // Router GEMM + softmax + top-k + renormalisation.
@@ -110,7 +111,7 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
 hipError_t launch_gemm_prefill(GemmKind kind, const GemmArgs &a, hipStream_t s);
 // Router logits of long batches on the compute-bound kernel: partials[p][t][e]
 // = sum over the p-th of `splits` equal K ranges of x[t] . wr[e] (fp32);
-// logits_splits picks `splits` for a shape.
+// logits_splits picks `splits` (at most kMaxLogitSplits) for a shape.
 int logits_splits(int T, int h, int E);
 hipError_t launch_logits_gemm(const uint16_t *x, const uint16_t *wr, int T, int h, int E,
                               float *partials, int splits, hipStream_t s);

@@ -30,6 +30,12 @@ __device__ __forceinline__ unsigned long long topk_key(float v, int e) {
          static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(e));
 }
 
+// The logit a key was made from (-0 comes back as +0).
+__device__ __forceinline__ float topk_key_value(unsigned long long key) {
+  const uint32_t u = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -57,8 +63,15 @@ __device__ void topk_rows(const float *sl, float *selv, int t0, int T,
     if (t >= T) break;
     const float *row = sl + static_cast<int64_t>(tt) * E;
     auto logit = [&](int e) {
-      float v = row[e];
-      for (int pl = 1; pl < planes; ++pl) v += row[pl * plane + e];
+      // all plane loads first, then the sum in plane order
+      float part[kMaxLogitSplits];
+#pragma unroll
+      for (int pl = 0; pl < kMaxLogitSplits; ++pl)
+        part[pl] = pl < planes ? row[pl * plane + e] : 0.0f;
+      float v = part[0];
+#pragma unroll
+      for (int pl = 1; pl < kMaxLogitSplits; ++pl)
+        if (pl < planes) v += part[pl];
       if (bias) v += bias[e];
       return v;
     };
@@ -79,7 +92,7 @@ __device__ void topk_rows(const float *sl, float *selv, int t0, int T,
         if (lane + 64 * c == e) key[c] = 0;
       if (lane == 0) {
         ids[static_cast<int64_t>(t) * k + j] = e;
-        mysel[j] = logit(e);
+        mysel[j] = topk_key_value(best);
       }
     }
     __builtin_amdgcn_wave_barrier();
