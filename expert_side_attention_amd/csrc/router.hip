@@ -8,8 +8,10 @@
 // "一个在啃带宽，一个在吃算力"); the softmax, the tie rule and the
 // renormalisation are this library's reading of that step.
 //
-// bf16 path: see router_bf16_kernel.  fp32 path (small layers): one dot
-// product per thread, one workgroup per 16 tokens.
+// bf16 path: router_bf16_kernel up to 4096 tokens, above that the logits
+// mode of the compute-bound GEMM (split-K partial planes); topk_kernel then
+// selects.  fp32 path (small layers): one dot product per thread, one
+// workgroup per 16 tokens, top-k in the same kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,8 +19,9 @@ namespace afd {
 namespace {
 
 // bf16 batches above this many tokens take the LDS-tiled logits GEMM (at
-// 8192 tokens of DeepSeek-V3 width it takes the router from 153 to 90 us; at
-// 2048 the register-operand kernel below is faster, 55 against 76 us)
+// 8192 tokens of DeepSeek-V3 width logits plus top-k went from 153 to 90 us,
+// 74 us with the top-k's loads hoisted; at 2048 the register-operand kernel
+// below is faster, 55 against 76 us)
 constexpr int kTiledRouterT = 4096;
 
 // Sortable key: larger logit first, then smaller index.  Key 0 = removed.

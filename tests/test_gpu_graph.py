@@ -28,6 +28,8 @@ def _layer(shape, seed):
     LayerShape("graph_bf16", T=128, h=256, E=16, k=4, I=256, S=1, Is=256, mode="bf16"),
     LayerShape("graph_w8a8", T=96, h=256, E=8, k=2, I=256, S=1, Is=128, mode="w8a8"),
     LayerShape("graph_prefill", T=1200, h=256, E=4, k=2, I=256, S=1, Is=128, mode="bf16"),
+    # the tiled router (two K splits) under capture
+    LayerShape("graph_router_tiled", T=4200, h=1024, E=64, k=2, I=128, mode="bf16"),
 ], ids=lambda s: s.name)
 def test_graph_replay_matches_eager(shape):
     layer, x = _layer(shape, seed=11)
