@@ -67,6 +67,10 @@ SMALL = [
     LayerShape("bf16_many_experts", T=77, h=512, E=64, k=8, I=256, S=2, Is=128, mode="bf16"),
     LayerShape("bf16_e256", T=40, h=128, E=256, k=8, I=128, mode="bf16"),
     LayerShape("bf16_e512", T=20, h=128, E=512, k=4, I=128, S=1, Is=128, mode="bf16"),
+    # an expert count that fills no 16-expert router slice, odd k
+    LayerShape("bf16_odd_e", T=150, h=256, E=37, k=5, I=256, S=1, Is=128, mode="bf16"),
+    # the most shared experts the library takes
+    LayerShape("bf16_s8", T=64, h=128, E=8, k=2, I=128, S=8, Is=128, mode="bf16"),
     # enough 64-row work items for the 8-wave gate/up shape, 512-byte down stages
     LayerShape("bf16_e256_wide", T=512, h=256, E=256, k=8, I=1024, S=1, Is=1024, mode="bf16"),
     LayerShape("bf16_zipf", T=500, h=256, E=32, k=4, I=128, S=1, Is=128, mode="bf16",
