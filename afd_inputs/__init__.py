@@ -83,6 +83,14 @@ CONFIGS = {
                                       E=256, k=8, I=2048, S=1, Is=2048,
                                       mode="bf16", router="zipf",
                                       micro_batches=2),
+    # One GPU's share of the two DeepSeek-V3 decode layers under 8-way expert
+    # parallelism: 32 local experts, the T*k/8 dispatched rows that arrive
+    # (one local expert each), no shared expert (it stays with the tokens).
+    "dsv3_ep8_shard_t512": LayerShape("dsv3_ep8_shard_t512", T=512, h=7168,
+                                      E=32, k=1, I=2048, mode="bf16"),
+    "dsv3_w8a8_ep8_shard_t2048": LayerShape("dsv3_w8a8_ep8_shard_t2048", T=2048,
+                                            h=7168, E=32, k=1, I=2048,
+                                            mode="w8a8"),
 }
 
 
