@@ -111,3 +111,11 @@ def test_dsv3_w8a8_t2048():
 
 def test_prefill_skew_two_microbatches():
     check_full("prefill_skew_t16384", microbatches=2, n_sample=16)
+
+
+def test_dsv3_ep8_shard():
+    check_full("dsv3_ep8_shard_t512")
+
+
+def test_dsv3_w8a8_ep8_shard():
+    check_full("dsv3_w8a8_ep8_shard_t2048")
