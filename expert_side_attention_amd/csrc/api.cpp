@@ -39,6 +39,9 @@ int hip_fail(hipError_t e, const char *what) {
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+// The kernels move activations, weights and outputs in 16-byte pieces and
+// read biases and scales as floats.
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 struct StageEvents {
   hipEvent_t start, stop;
@@ -136,6 +139,14 @@ int validate_weights(const afd_ffn_config *c, const afd_ffn_weights *w) {
     if (fp8 && (!w->sh_gate_s || !w->sh_up_s || !w->sh_down_s))
       return fail(AFD_ERR_INVALID_ARG, "W8A8 with shared experts needs sh_*_s");
   }
+  const void *mats[] = {w->router_w, w->gate_w, w->up_w, w->down_w,
+                        w->sh_gate_w, w->sh_up_w, w->sh_down_w};
+  for (const void *m : mats)
+    if (!aligned(m, 16)) return fail(AFD_ERR_INVALID_ARG, "weight matrices must be 16-byte aligned");
+  const void *floats[] = {w->router_b, w->gate_s, w->up_s, w->down_s,
+                          w->sh_gate_s, w->sh_up_s, w->sh_down_s};
+  for (const void *f : floats)
+    if (!aligned(f, 4)) return fail(AFD_ERR_INVALID_ARG, "router_b and scales must be 4-byte aligned");
   return AFD_OK;
 }
 
@@ -290,6 +301,8 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
                 c.max_tokens);
   if (T == 0) return AFD_OK;
   if (!hidden || !out) return fail(AFD_ERR_INVALID_ARG, "hidden and out must not be NULL");
+  if (!aligned(hidden, 16) || !aligned(out, 16))
+    return fail(AFD_ERR_INVALID_ARG, "hidden and out must be 16-byte aligned");
   const int aes = h->elem == 0 ? 4 : 2;
   const size_t act_bytes = static_cast<size_t>(T) * c.hidden * aes;
   const char *hb = static_cast<const char *>(hidden);
@@ -466,6 +479,8 @@ int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out, int
 int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols, uint8_t *q, float *s,
                         afd_stream_t stream) {
   if (!x || !q || !s) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4))
+    return fail(AFD_ERR_INVALID_ARG, "x and q must be 16-byte aligned, s 4-byte aligned");
   if (rows < 0 || cols <= 0 || cols % 128)
     return fail(AFD_ERR_INVALID_ARG, "rows >= 0 and cols a positive multiple of 128 required");
   if (rows == 0) return AFD_OK;
@@ -479,6 +494,8 @@ int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols, uint8_t *q, f
 int afd_quant_fp8_1x128_f32(const float *x, int64_t rows, int64_t cols, uint8_t *q, float *s,
                             afd_stream_t stream) {
   if (!x || !q || !s) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4))
+    return fail(AFD_ERR_INVALID_ARG, "x and q must be 16-byte aligned, s 4-byte aligned");
   if (rows < 0 || cols <= 0 || cols % 128)
     return fail(AFD_ERR_INVALID_ARG, "rows >= 0 and cols a positive multiple of 128 required");
   if (rows == 0) return AFD_OK;
@@ -492,6 +509,8 @@ int afd_quant_fp8_1x128_f32(const float *x, int64_t rows, int64_t cols, uint8_t 
 int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols, uint8_t *q, float *s,
                           afd_stream_t stream) {
   if (!w || !q || !s) return fail(AFD_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(s, 4))
+    return fail(AFD_ERR_INVALID_ARG, "w and q must be 16-byte aligned, s 4-byte aligned");
   if (rows <= 0 || cols <= 0 || rows % 128 || cols % 128)
     return fail(AFD_ERR_INVALID_ARG, "rows and cols must be positive multiples of 128");
   if ((rows / 128) * (cols / 128) >= (1LL << 31))

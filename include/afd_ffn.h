@@ -55,7 +55,8 @@ typedef void *afd_stream_t; /* a hipStream_t */
 
 typedef enum {
   AFD_OK = 0,
-  AFD_ERR_INVALID_ARG = 1,   /* NULL, aliasing, bad size, bad config        */
+  AFD_ERR_INVALID_ARG = 1,   /* NULL, aliasing, misalignment, bad size,
+                                bad config                                  */
   AFD_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels handle   */
   AFD_ERR_CAPACITY = 3,      /* T > max_tokens given at create()            */
   AFD_ERR_OUT_OF_MEMORY = 4, /* workspace allocation failed in create()     */
@@ -94,7 +95,9 @@ typedef struct {
  *   down_w [E, h, I]          as gate_w
  *   gate_s, up_s [E, I/128, h/128], down_s [E, h/128, I/128]
  *                             fp32 block scales, W8A8 only (else ignored)
- *   sh_* : the same for the S shared experts with I_s in place of I.      */
+ *   sh_* : the same for the S shared experts with I_s in place of I.
+ * Weight matrices must be 16-byte aligned, router_b and the scales 4-byte
+ * aligned (create() returns AFD_ERR_INVALID_ARG otherwise).               */
 typedef struct {
   const void *router_w;
   const float *router_b;
@@ -134,8 +137,8 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
                    afd_ffn_handle **out);
 
 /* out[T, h] = MoE-FFN(hidden[T, h]).  hidden/out: fp32 in F32 mode, bf16
- * otherwise; they must not overlap.  0 <= T <= max_tokens (T = 0 is a
- * no-op).  Asynchronous on `stream`; the handle's workspace is in use until
+ * otherwise, 16-byte aligned; they must not overlap.  0 <= T <= max_tokens
+ * (T = 0 is a no-op).  Asynchronous on `stream`; the handle's workspace is in use until
  * the enqueued work completes.                                            */
 int afd_ffn_forward(afd_ffn_handle *h, const void *hidden, void *out,
                     int64_t T, afd_stream_t stream);
@@ -152,7 +155,7 @@ void afd_ffn_destroy(afd_ffn_handle *h);
 /* FP8 E4M3 activation quantiser: one scale per row per 128 columns.
  * x [rows, cols] bf16 -> q [rows, cols] E4M3 bytes, s [rows, cols/128] fp32,
  * s = fl32(amax/448) (1 if that is 0), q = RNE-saturating E4M3 of
- * fl32(x/s).  cols % 128 == 0.                                            */
+ * fl32(x/s).  cols % 128 == 0; x and q 16-byte aligned, s 4-byte.       */
 int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols,
                         uint8_t *q, float *s, afd_stream_t stream);
 
@@ -160,14 +163,16 @@ int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols,
  * SwiGLU output z between the two expert GEMMs (W8A8 is the precision of
  * the vLLM AFD plugin page's "效能基準測試").  x [rows, cols]
  * fp32 device array, row-major, contiguous; q, s as above; all three owned
- * by the caller.  Errors: NULL pointer or cols not a positive multiple of
- * 128 -> AFD_ERR_INVALID_ARG; rows = 0 is a no-op.                        */
+ * by the caller; x and q 16-byte aligned, s 4-byte.  Errors: NULL or
+ * misaligned pointer, or cols not a positive multiple of 128 ->
+ * AFD_ERR_INVALID_ARG; rows = 0 is a no-op.                               */
 int afd_quant_fp8_1x128_f32(const float *x, int64_t rows, int64_t cols,
                             uint8_t *q, float *s, afd_stream_t stream);
 
 /* FP8 E4M3 weight quantiser: one scale per 128x128 block, same rounding.
  * w [rows, cols] bf16 -> q [rows, cols], s [rows/128, cols/128].
- * rows % 128 == 0, cols % 128 == 0.  A stack [E, N, K] is rows = E*N.     */
+ * rows % 128 == 0, cols % 128 == 0.  A stack [E, N, K] is rows = E*N.
+ * w and q 16-byte aligned, s 4-byte.                                      */
 int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols,
                           uint8_t *q, float *s, afd_stream_t stream);
 

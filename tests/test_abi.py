@@ -91,6 +91,8 @@ def _w(**kw):
     ({}, dict(gate_w=None), F.AFD_ERR_INVALID_ARG, "gate_w"),
     (dict(mode=F.AFD_MODE_W8A8_E4M3), {}, F.AFD_ERR_INVALID_ARG, "gate_s"),
     (dict(num_shared=1, shared_inter=256), {}, F.AFD_ERR_INVALID_ARG, "sh_gate_w"),
+    ({}, dict(up_w=0x1008), F.AFD_ERR_INVALID_ARG, "16-byte aligned"),
+    (dict(has_router_bias=1), dict(router_b=0x1002), F.AFD_ERR_INVALID_ARG, "4-byte aligned"),
 ])
 def test_create_rejects_bad_config(lib, cfg, w, status, needle):
     with pytest.raises(F.AfdError) as ei:
@@ -110,5 +112,10 @@ def test_null_arguments_rejected(lib):
     assert lib.afd_quant_fp8_1x128(None, 4, 128, 1, 2, None) == F.AFD_ERR_INVALID_ARG
     assert lib.afd_quant_fp8_1x128(1, 4, 100, 1, 2, None) == F.AFD_ERR_INVALID_ARG
     assert lib.afd_quant_fp8_128x128(1, 100, 128, 1, 2, None) == F.AFD_ERR_INVALID_ARG
+    # misaligned buffers are refused before anything is launched
+    assert lib.afd_quant_fp8_1x128(0x1008, 4, 128, 0x2000, 0x3000, None) == F.AFD_ERR_INVALID_ARG
+    assert "aligned" in F.afd_ffn_last_error()
+    assert lib.afd_quant_fp8_1x128_f32(0x1000, 4, 128, 0x2000, 0x3002, None) == F.AFD_ERR_INVALID_ARG
+    assert lib.afd_quant_fp8_128x128(0x1000, 128, 128, 0x2004, 0x3000, None) == F.AFD_ERR_INVALID_ARG
     assert lib.afd_ffn_profile_enable(None, 1) == F.AFD_ERR_INVALID_ARG
     lib.afd_ffn_destroy(None)  # ignored

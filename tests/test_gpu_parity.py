@@ -276,6 +276,13 @@ def test_edge_token_counts_and_errors():
     with pytest.raises(AfdError) as ei:
         layer.forward(xt, out=xt)
     assert ei.value.status == 1  # aliasing
+    # a hidden pointer off the 16-byte grid is refused before any launch
+    from expert_side_attention_amd import _ffi as F
+    res = torch.empty_like(full)
+    with pytest.raises(AfdError) as ei:
+        F.afd_ffn_forward(layer._h, xt.data_ptr() + 2, res.data_ptr(), 1,
+                          torch.cuda.current_stream().cuda_stream)
+    assert ei.value.status == 1 and "aligned" in F.afd_ffn_last_error()
 
 
 def test_quantiser_all_bf16_values():
