@@ -69,6 +69,8 @@ SMALL = [
     LayerShape("bf16_e512", T=20, h=128, E=512, k=4, I=128, S=1, Is=128, mode="bf16"),
     # an expert count that fills no 16-expert router slice, odd k
     LayerShape("bf16_odd_e", T=150, h=256, E=37, k=5, I=256, S=1, Is=128, mode="bf16"),
+    # more slots than one combine pass gathers (eight at a time)
+    LayerShape("bf16_k16", T=40, h=128, E=64, k=16, I=128, S=1, Is=128, mode="bf16"),
     # the most shared experts the library takes
     LayerShape("bf16_s8", T=64, h=128, E=8, k=2, I=128, S=8, Is=128, mode="bf16"),
     # enough 64-row work items for the 8-wave gate/up shape, 512-byte down stages
