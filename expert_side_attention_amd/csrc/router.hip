@@ -8,9 +8,10 @@
 // "一个在啃带宽，一个在吃算力"); the softmax, the tie rule and the
 // renormalisation are this library's reading of that step.
 //
-// bf16 path: router_bf16_kernel up to 4096 tokens, above that the logits
-// mode of the compute-bound GEMM (split-K partial planes); topk_kernel then
-// selects.  fp32 path (small layers): one dot product per thread, one
+// bf16 path: router_bf16_kernel up to 4096 tokens (K split in four parts,
+// each with its own partial plane, for layers of at most 64 experts), above
+// that the logits mode of the compute-bound GEMM (split-K partial planes);
+// topk_kernel then adds the planes and selects.  fp32 path (small layers): one dot product per thread, one
 // workgroup per 16 tokens, top-k in the same kernel.
 #include "common.h"
 #include "kernels.h"
@@ -112,7 +113,9 @@ __device__ void topk_rows(const float *sl, float *selv, int t0, int T,
 }
 
 // bf16 router logits.  The grid is (expert slices of EN) x (token blocks of
-// TM), so even small batches spread over many CUs.  Inside a workgroup the
+// TM) x (K parts), so even small batches spread over many CUs; with more
+// than one K part each part writes its own partial plane and the top-k adds
+// the planes in order, then the bias.  Inside a workgroup the
 // WAVES waves take disjoint slices of h and compute all TM x EN partial
 // logits with operands loaded straight from global memory into MFMA
 // registers (no LDS, no barrier in the K loop, NBUF chunks of prefetch); the
@@ -130,9 +133,13 @@ __global__ __launch_bounds__(WAVES * 64) void router_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const int e0 = blockIdx.x * EN, t0 = blockIdx.y * TM;
-  const int kq = h / WAVES;     // this wave's K range [wave * kq, wave * kq + kq)
+  // K part blockIdx.z of gridDim.z: [z hs, z hs + hs), split over the waves;
+  // its partial logits go to plane z (T x E floats apart)
+  const int hs = h / static_cast<int>(gridDim.z);
+  const int kq = hs / WAVES;    // this wave's K range [wave * kq, wave * kq + kq) of the part
   const int nchunks = kq / 32;  // 32 K elements per MFMA
-  const int kbase = wave * kq + q * 8;
+  const int kbase = static_cast<int>(blockIdx.z) * hs + wave * kq + q * 8;
+  logits += static_cast<int64_t>(blockIdx.z) * T * E;
 
   const uint16_t *arow[MB];
   bool avalid[MB];
@@ -245,6 +252,12 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 
 }  // namespace
 
+// K parts of the register router: with at most 64 experts a batch has few
+// expert slices, so the K range is split in four over workgroups to spread
+// the operand reads over more CUs.  A function of the layer shape only, so
+// a token's logits do not depend on the batch it came in.
+int router_k_parts(int h, int E) { return E <= 64 && h % (4 * 256) == 0 ? 4 : 1; }
+
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
                          float *logits, int32_t *ids, float *w, hipStream_t s) {
@@ -276,9 +289,11 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
   // token blocks of 16 (32 above 1024 tokens), expert slices sized so that
   // a batch launches a few hundred workgroups, K split over 8 waves (4 when
   // h is not a multiple of 256)
+  const int parts = router_k_parts(h, E);
+  const float *kbias = parts == 1 ? bias : nullptr;
 #define AFD_ROUTER(TM, EN, NBUF, WAVES)                                                 \
   router_bf16_kernel<TM, EN, NBUF, WAVES>                                              \
-      <<<dim3((E + EN - 1) / EN, (T + TM - 1) / TM), WAVES * 64, 0, s>>>(X, W, bias, T, h, \
+      <<<dim3((E + EN - 1) / EN, (T + TM - 1) / TM, parts), WAVES * 64, 0, s>>>(X, W, kbias, T, h, \
                                                                            E, logits)
   // each wave's K slice must be whole 32-element chunks: 8 waves need
   // h % 256 == 0, 4 waves h % 128 == 0 (always true here)
@@ -299,12 +314,11 @@ hipError_t launch_router(bool f32, const void *x, const void *wr,
 #undef AFD_ROUTER
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return topk(1, nullptr);
+  return parts == 1 ? topk(1, nullptr) : topk(parts, bias);
 }
 
 int64_t router_logit_floats(int T, int h, int E) {
-  (void)h;
-  if (T <= kTiledRouterT) return static_cast<int64_t>(T) * E;
+  if (T <= kTiledRouterT) return static_cast<int64_t>(router_k_parts(h, E)) * T * E;
   // tiled path, t tokens: splits <= 16, and either splits = 1 or
   // splits x row tiles <= 256 with t <= 256 x row tiles, so the planes hold
   // splits x t <= max(t, min(16 t, 65536)) rows
