@@ -78,6 +78,10 @@ SMALL = [
     LayerShape("bf16_zipf", T=500, h=256, E=32, k=4, I=128, S=1, Is=128, mode="bf16",
                router="zipf"),
     LayerShape("bf16_big_t", T=2100, h=128, E=64, k=2, I=128, mode="bf16"),
+    # the register router with its K range in four partial planes (at most 64
+    # experts, h a multiple of 1024), the bias added by the top-k after them
+    LayerShape("bf16_kparts_zipf", T=300, h=1024, E=48, k=6, I=128, S=1, Is=128, mode="bf16",
+               router="zipf"),
     LayerShape("bf16_e512_blocks", T=2049, h=128, E=512, k=8, I=128, S=1, Is=128,
                mode="bf16"),
     LayerShape("f32_k_eq_e", T=70, h=128, E=4, k=4, I=128, S=1, Is=256, mode="f32"),
