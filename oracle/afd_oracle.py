@@ -44,8 +44,11 @@ library routine; uniform-logit mean-of-experts case; sum of weights; brute
 force subset enumeration for top-k; exact ties; naive dispatch enumeration
 and dispatch invariants; the full E4M3 code table against the OCP formula
 and the codec's rounding/saturation rules; quantiser scale and block-index
-checks; W8A8 error band against the unquantised layer.  No function here is
-left unpinned.
+checks; the W8A8 re-quantisation of z bit for bit against a brute-force
+rebuild from the E4M3 definition (with identity down weights, also through
+the whole layer), with planted mistakes in that step shown to fail; W8A8
+error band against the unquantised layer.  No function here is left
+unpinned.
 """
 from __future__ import annotations
 

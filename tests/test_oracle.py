@@ -371,6 +371,137 @@ def test_w8a8_error_band():
     assert np.array_equal(res["x_q"], q) and np.array_equal(res["x_s"], s)
 
 
+def _e4m3_grid_from_definition():
+    """Finite non-negative E4M3FN values built from the format's definition
+    (4 exponent bits with bias 7, 3 mantissa bits, subnormals at exponent
+    field 0, exponent 15 with mantissa 7 reserved for NaN); index == code."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            vals.append((m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def _requantised_z_brute(z64):
+    """What the W8A8 layer feeds its down product, rebuilt step by step
+    without the oracle's quantiser: z rounded to fp32; per row, groups of 128
+    consecutive channels; s = fp32 quotient amax / 448 (1 if that is 0);
+    each element divided by s in fp32 and replaced by the nearest E4M3 value
+    (ties to the even code, saturating at 448); value = code value * s."""
+    grid = _e4m3_grid_from_definition()
+    z32 = np.asarray(z64, np.float64).astype(np.float32)
+    out = np.empty(z32.shape, np.float64)
+    for r in range(z32.shape[0]):
+        for g0 in range(0, z32.shape[1], 128):
+            grp = z32[r, g0:g0 + 128]
+            amax = np.float32(np.max(np.abs(grp)))
+            s = np.float32(amax / np.float32(448.0))
+            if amax == 0 or s == 0:
+                s = np.float32(1.0)
+            v = (grp / s).astype(np.float32).astype(np.float64)
+            a = np.minimum(np.abs(v), 448.0)
+            d = np.abs(a[:, None] - grid[None, :])
+            best = d.min(axis=1, keepdims=True)
+            cand = d == best
+            # among equally near grid values take the even code
+            code = np.where(cand & (np.arange(len(grid)) % 2 == 0)[None, :],
+                            np.arange(len(grid))[None, :], 10 ** 6).min(axis=1)
+            code = np.where(cand.sum(axis=1) == 1, d.argmin(axis=1), code)
+            out[r, g0:g0 + 128] = np.copysign(grid[code], v) * np.float64(s)
+    return out
+
+
+def _z_pin_holds(swiglu_fn):
+    """D = identity, so swiglu(quant_z=True) must return the re-quantised z
+    itself, bit for bit.  Rows and groups span several orders of magnitude so
+    that a scale taken over the wrong set of elements changes the result."""
+    g = np.random.default_rng(31)
+    n, h = 256, 256
+    x = O.bf16_to_f64(f32_to_bf16_bits(g.standard_normal((n, h)).astype(np.float32)))
+    x *= (2.0 ** g.integers(-6, 4, size=(n, 1)))
+    G = O.bf16_to_f64(f32_to_bf16_bits((g.standard_normal((h, h)) * 0.05).astype(np.float32)))
+    U = O.bf16_to_f64(f32_to_bf16_bits((g.standard_normal((h, h)) * 0.05).astype(np.float32)))
+    U[128:] *= 64.0                                   # second channel group much larger
+    D = np.eye(h)
+    got = swiglu_fn(x, G, U, D, quant_z=True)
+    xt = torch.from_numpy(x)
+    z = (F.silu(xt @ torch.from_numpy(G).T) * (xt @ torch.from_numpy(U).T)).numpy()
+    return np.array_equal(got, _requantised_z_brute(z))
+
+
+def test_w8a8_z_requantisation_step():
+    """The W8A8 re-quantisation of z between the two expert products (W8A8
+    precision: vLLM AFD plugin page, "效能基準測試"), pinned bit for bit
+    against a brute-force rebuild from the E4M3 definition."""
+    assert _z_pin_holds(O.swiglu)
+
+
+def _mutant_no_requant(xr, G, U, D, quant_z=False):
+    return (O.silu(xr @ G.T) * (xr @ U.T)) @ D.T
+
+
+def _mutant_wrong_axis(xr, G, U, D, quant_z=False):
+    z = O.silu(xr @ G.T) * (xr @ U.T)
+    q, s = O.quantize_1x128(z.astype(np.float32).T)   # groups of 128 tokens
+    return O.dequantize_1x128(q, s).T @ D.T
+
+
+def _mutant_no_fp32_rounding(xr, G, U, D, quant_z=False):
+    z = O.silu(xr @ G.T) * (xr @ U.T)                 # scale from the fp64 z
+    R, C = z.shape
+    grp = z.reshape(R, C // 128, 128)
+    s = (np.abs(grp).max(axis=2) / 448.0).astype(np.float32)
+    v = (grp / s[..., None].astype(np.float64)).astype(np.float32)
+    q = O.e4m3_encode(v).reshape(R, C)
+    return O.dequantize_1x128(q, s) @ D.T
+
+
+def _mutant_fp64_scale(xr, G, U, D, quant_z=False):
+    z = (O.silu(xr @ G.T) * (xr @ U.T)).astype(np.float32).astype(np.float64)
+    R, C = z.shape
+    grp = z.reshape(R, C // 128, 128)
+    s = np.abs(grp).max(axis=2) / 448.0               # scale never rounded to fp32
+    v = (grp / s[..., None]).astype(np.float32)
+    q = O.e4m3_encode(v).reshape(R, C)
+    return (O._decode_fast(q).reshape(R, C // 128, 128) * s[..., None]).reshape(R, C) @ D.T
+
+
+@pytest.mark.parametrize("mutant", [_mutant_no_requant, _mutant_wrong_axis,
+                                    _mutant_no_fp32_rounding, _mutant_fp64_scale],
+                         ids=["no_requant", "wrong_axis", "no_fp32_rounding", "fp64_scale"])
+def test_w8a8_z_pin_rejects_planted_mistakes(mutant):
+    """Each plausible mistake in the z step, planted in a copy of the
+    oracle's function, fails the pin above."""
+    assert not _z_pin_holds(mutant)
+
+
+def test_w8a8_layer_applies_z_step():
+    """E = 1, k = 1, W8A8 with D = (7/16) I: a block scale of exactly 2^-10
+    and codes of exactly 448 make the quantised D equal D, so the layer
+    output is 7/16 times the re-quantised z of the quantised input and gate /
+    up weights (those quantisers are pinned above).  Fails if the layer
+    skips, misplaces or changes the z step."""
+    shp = _small_shape(T=16, h=256, I=256, mode="w8a8")
+    L = SyntheticLayer(shp, seed=13)
+    G, U, _ = L.expert(0)
+    D = f32_to_bf16_bits(np.eye(256, dtype=np.float32) * np.float32(0.4375))
+    src = ArraySource(shp, L.router_weight(), None, [(G, U, D)])
+    x = L.hidden()
+    out = O.OracleFFN(src).forward(x)["out"]
+    q, s = O.quantize_1x128(O.bf16_to_f64(x).astype(np.float32))
+    xq = torch.from_numpy(O.dequantize_1x128(q, s))
+
+    def deq(m):
+        qq, ss = O.quantize_128x128(O.bf16_to_f64(m).astype(np.float32))
+        return torch.from_numpy(O.dequantize_128x128(qq, ss))
+
+    assert torch.equal(deq(D), torch.from_numpy(O.bf16_to_f64(D)))
+    z = (F.silu(xq @ deq(G).T) * (xq @ deq(U).T)).numpy()
+    assert np.array_equal(out, 0.4375 * _requantised_z_brute(z))
+
+
 # ---------------------------------------------------------------- pages' figure
 def test_comm_volume_figure_from_pages():
     """The A/F page's traffic example (h = 4096, k = 8, FP8) prints about
