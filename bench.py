@@ -4,11 +4,20 @@ One step = one forward of the whole layer (router + top-k, dispatch,
 [quantise], gate/up GEMM + SwiGLU, down GEMM, shared expert, combine) over
 one batch of seeded synthetic hidden states already resident in HBM.
 
-Default workload: decode micro-batch T=256, h=4096, E=64 routed experts,
-top-8, SwiGLU intermediate 1536, one shared expert (1536), bf16 with fp32
-accumulation.  Prints one JSON line.  Extra fields: "roofline" of the
-dominant kernel (gate/up GEMM, timed with HIP events on the forward's stream
-over the timed region) and "cpu_baseline" (the fp64 oracle on the host).
+Default workload: the prefill chunk with skewed routing, T = 16384 tokens in
+two micro-batches of 8192 on two HIP streams, h = 7168, E = 256 routed
+experts, top-8, SwiGLU intermediate 2048, one shared expert (2048), bf16
+with fp32 accumulation, router logits N(0, 1) + log of a Zipf(1.2) share.
+Prints one JSON line.  Extra fields: "roofline" of the dominant kernel and
+"cpu_baseline" (the fp64 oracle on the host, on a bounded sample).
+
+Roofline: weight-streaming layers (one micro-batch) time the gate/up launch
+with HIP events on the forward's stream over the timed region, against the
+algorithmic bytes of the touched experts.  The two-micro-batch prefill layer
+times its compute-bound gate/up launch (256-row tiles) with HIP events in a
+serial pass after the timed region (micro-batches back to back on one
+stream, so no other kernel shares the interval), against the unpadded flops
+of the rows in those tiles.
 """
 from __future__ import annotations
 
@@ -25,7 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-FFN layer tokens/s on 1 MI355X + % of HBM-BW / MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "w8a8": 5000.0, "f32": 157.3}
-DEFAULT_WORKLOAD = "decode_h4096_e64"
+DEFAULT_WORKLOAD = "prefill_skew_t16384"
 
 
 def log(msg):
@@ -87,27 +96,68 @@ def work_model(s, counts):
     }
 
 
+def big_tile_rows(s, counts, T):
+    """Rows the forward sends to the compute-bound kernel (256-row tiles) and
+    the number of those tiles, per group (routed experts, then shared).
+
+    The library's tile plan: bf16 batches averaging more than 112 rows per
+    expert give every group of at least 129 rows its full 256-row tiles, plus
+    one partial tile when the remainder exceeds 128 rows; the rest stays on
+    the weight-streaming kernel.  The tile count is checked against the
+    library's own (traced) count, so a change of plan cannot go unnoticed."""
+    if s.mode != "bf16" or -(-T * s.k // s.E) <= 112:
+        return [0] * (s.E + s.S), 0
+    rows, tiles = [], 0
+    for gc in list(counts) + [T] * s.S:
+        nbig, rem = 0, gc
+        if gc >= 129:
+            nbig, rem = gc // 256, gc % 256
+            if rem * 2 > 256:
+                nbig, rem = nbig + 1, 0
+        rows.append(gc - rem)
+        tiles += nbig
+    return rows, tiles
+
+
 def work_model_microbatches(s, layers, xs):
     """Sum of the per-micro-batch models: each micro-batch streams the
-    weights of the experts it touches."""
+    weights of the experts it touches.  Also the unpadded flops of the
+    compute-bound gate/up launch, per launch."""
+    import torch
     tot = None
+    big_flops = []
     for li, xi in zip(layers, xs):
         _, tr = li.forward(xi, trace=True)
-        import torch
         torch.cuda.synchronize()
-        m = work_model(s.with_tokens(xi.shape[0]), tr["counts"].cpu().tolist())
+        counts = tr["counts"].cpu().tolist()
+        sm = s.with_tokens(xi.shape[0])
+        m = work_model(sm, counts)
+        rows, tiles = big_tile_rows(sm, counts, xi.shape[0])
+        lib_tiles = int(tr["num_tiles"][1].item())
+        if tiles != lib_tiles:
+            raise RuntimeError(f"tile plan mismatch: {tiles} compute-bound tiles predicted, "
+                               f"the library made {lib_tiles}")
+        big_flops.append(sum(2 * r * 2 * (s.I if g < s.E else s.Is) * s.h
+                             for g, r in enumerate(rows)))
         if tot is None:
             tot = dict(m)
         else:
             for kk in ("gate_up_bytes", "gate_up_flops", "forward_bytes", "forward_flops"):
                 tot[kk] += m[kk]
             tot["touched_experts"] = max(tot["touched_experts"], m["touched_experts"])
+    tot["gate_up_big_flops"] = big_flops
     return tot
 
 
-def cpu_baseline(syn, min_seconds=10.0):
-    """The fp64 oracle on the same batch, weights pre-drawn in host memory."""
+def cpu_baseline(syn, min_seconds=10.0, max_tokens=512):
+    """The fp64 oracle on host cores.  Small layers: the whole batch, repeated
+    for at least min_seconds.  Large layers: a bounded sample, the first
+    max_tokens tokens of the batch (routed the same way as in the full
+    batch, since a token's routing does not depend on the others), once or
+    more until min_seconds.  The weights of the experts the sample touches
+    are drawn into host memory before the clock starts."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import afd_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -115,8 +165,9 @@ def cpu_baseline(syn, min_seconds=10.0):
     except Exception:  # pragma: no cover
         blas_threads = 1
     s = syn.shape
-    g, u, d = syn.stacked_experts()
-    sh = syn.stacked_shared()
+    cores = len(os.sched_getaffinity(0))
+    n = s.T if s.T * s.h * s.E <= 256 * 4096 * 64 else min(s.T, max_tokens)
+    x = syn.hidden()[:n]
     wr, b = syn.router_weight(), syn.router_bias()
 
     class Src:
@@ -129,26 +180,31 @@ def cpu_baseline(syn, min_seconds=10.0):
             return b
 
         def expert(self, e):
-            return g[e], u[e], d[e]
+            return experts[e]
 
         def shared(self, j):
-            return sh[0][j], sh[1][j], sh[2][j]
+            return shared[j]
 
+    # routing of the sample (untimed) tells which experts to draw
+    ids = O.OracleFFN(Src()).route(x)[1]
+    touched = sorted(set(np.unique(ids).tolist()))
+    with ThreadPoolExecutor(max_workers=max(1, min(16, cores))) as ex:
+        experts = dict(zip(touched, ex.map(syn.expert, touched)))
+        shared = list(ex.map(syn.shared, range(s.S)))
     orc = O.OracleFFN(Src())
-    x = syn.hidden()
     tokens, t0 = 0, time.perf_counter()
     while True:
         orc.forward(x)
-        tokens += s.T
+        tokens += n
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    cores = len(os.sched_getaffinity(0))
+    what = (f"full {s.name} batch of {n} tokens" if n == s.T else
+            f"first {n} of the {s.T} tokens of {s.name} ({len(touched)} experts touched)")
     return {"value": tokens / el, "unit": "tokens/s", "cores": int(min(cores, blas_threads)),
             "kind": "oracle",
-            "sample": f"full {s.name} batch of {s.T} tokens, {tokens // s.T} pass(es), "
-                      f"{el:.1f} s; fp64 NumPy/OpenBLAS, weights pre-drawn in host RAM; "
-                      f"host has {cores} cores"}
+            "sample": f"{what}, {tokens // n} pass(es), {el:.1f} s; fp64 NumPy/OpenBLAS, "
+                      f"weights drawn into host RAM before timing; host has {cores} cores"}
 
 
 def pipeline(args):
@@ -273,8 +329,29 @@ def main():
     ms_step = (t1 - t0) * 1e3 / args.steps
     gu_avg = gu_ms / max(gu_n, 1)
 
+    # two micro-batches: the dominant (compute-bound gate/up) launch timed in
+    # a serial pass, so that no kernel of the other stream shares its
+    # interval
+    big_avg = None
+    if nmb > 1:
+        for li in layers:
+            li.profile_enable(["gate_up_big"])
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            for li, xi, oi in zip(layers, xs, outs):
+                li.forward(xi, out=oi)
+        torch.cuda.synchronize()
+        b_ms = b_n = 0
+        for li in layers:
+            prof = li.profile_read()
+            li.profile_enable([])
+            b_ms += prof["gate_up_big"][0]
+            b_n += prof["gate_up_big"][1]
+        big_avg = b_ms / max(b_n, 1)
+
     # untimed breakdown of all stages, one micro-batch at a time
-    all_stages = ["router", "dispatch", "quant", "gate_up", "down", "combine"]
+    all_stages = ["router", "dispatch", "quant", "gate_up", "down", "combine", "gate_up_big",
+                  "down_big"]
     stage_tot = {}
     for li in layers:
         li.profile_enable(all_stages)
@@ -329,7 +406,6 @@ def main():
     ridge = MFMA_PEAK_TFLOPS[shape.mode] * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "mfma" if ai > ridge else "hbm"
     gu_launch_bytes = model["gate_up_bytes"] / nmb
-    gu_launch_flops = model["gate_up_flops"] / nmb
     achieved = gu_launch_bytes / (gu_avg * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{shape.name}.json")
@@ -339,6 +415,30 @@ def main():
         if t.get("kernel_source_hash") == kernel_source_hash():
             traffic = t.get("hbm_bytes_per_launch")
     res_hash = kernel_source_hash()
+    if bound == "hbm":
+        roofline = {"bound": "hbm", "kernel": "gate_up grouped GEMM + SwiGLU (weight streaming)",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "avg_launch_ms": round(gu_avg, 5),
+                    "algorithmic_bytes_per_launch": int(gu_launch_bytes),
+                    "timed": "HIP events around each gate/up launch in the timed region"}
+    else:
+        # compute-bound gate/up launch: unpadded flops of its rows, averaged
+        # over the micro-batches' launches (one per micro-batch per step)
+        flops = sum(model["gate_up_big_flops"]) / nmb
+        avg = big_avg if big_avg is not None else gu_avg
+        if flops <= 0:
+            raise RuntimeError("compute-bound layer without compute-bound tiles")
+        tf = flops / (avg * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[shape.mode]
+        roofline = {"bound": "mfma",
+                    "kernel": "gate_up grouped GEMM + SwiGLU, 256-row tiles (prefill_gemm_kernel<1>)",
+                    "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tf / peak, 4), "traffic": traffic,
+                    "avg_launch_ms": round(avg, 5),
+                    "algorithmic_flops_per_launch": int(flops),
+                    "timed": ("HIP events around each compute-bound gate/up launch, serial pass "
+                              f"of {args.steps} steps after the timed region")}
     value = shape.T / (ms_step * 1e-3)
     fwd_gbs = model["forward_bytes"] / (ms_step * 1e-3) / 1e9
     res = {
@@ -357,19 +457,7 @@ def main():
         "config": {"workload": shape.name, "T": shape.T, "h": shape.h, "E": shape.E,
                    "k": shape.k, "I": shape.I, "S": shape.S, "Is": shape.Is,
                    "mode": shape.mode, "seed": args.seed},
-        "roofline": ({"bound": "hbm", "kernel": "gate_up grouped GEMM + SwiGLU",
-                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                      "avg_launch_ms": round(gu_avg, 5),
-                      "algorithmic_bytes_per_launch": int(gu_launch_bytes)}
-                     if bound == "hbm" else
-                     {"bound": "mfma", "kernel": "gate_up grouped GEMM + SwiGLU",
-                      "achieved": round(gu_launch_flops / (gu_avg * 1e-3) / 1e12, 2),
-                      "peak": MFMA_PEAK_TFLOPS[shape.mode], "unit": "TFLOP/s",
-                      "frac": round(gu_launch_flops / (gu_avg * 1e-3) / 1e12
-                                    / MFMA_PEAK_TFLOPS[shape.mode], 4),
-                      "traffic": traffic, "avg_launch_ms": round(gu_avg, 5),
-                      "algorithmic_flops_per_launch": int(gu_launch_flops)}),
+        "roofline": roofline,
         "forward": {"hbm_gbs": round(fwd_gbs, 1), "hbm_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
                     "bytes": int(model["forward_bytes"]),
                     "tflops": round(model["forward_flops"] / (ms_step * 1e-3) / 1e12, 2),

@@ -15,11 +15,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libafd_ffn.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "afd_ffn.h")
 
-AFD_FFN_ABI_VERSION = 1
+AFD_FFN_ABI_VERSION = 2
 AFD_OK, AFD_ERR_INVALID_ARG, AFD_ERR_UNSUPPORTED = 0, 1, 2
 AFD_ERR_CAPACITY, AFD_ERR_OUT_OF_MEMORY, AFD_ERR_HIP = 3, 4, 5
 AFD_MODE_F32, AFD_MODE_BF16, AFD_MODE_W8A8_E4M3 = 0, 1, 2
-STAGES = ("router", "dispatch", "quant", "gate_up", "down", "combine")
+STAGES = ("router", "dispatch", "quant", "gate_up", "down", "combine", "gate_up_big",
+          "down_big")
 STAGE_INDEX = {n: i for i, n in enumerate(STAGES)}
 
 _STATUS_NAMES = {0: "AFD_OK", 1: "AFD_ERR_INVALID_ARG", 2: "AFD_ERR_UNSUPPORTED",
@@ -50,7 +51,7 @@ class afd_ffn_weights(ctypes.Structure):
 class afd_ffn_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_ids", "topk_w", "counts", "offsets", "perm", "slot_row", "x_q",
-        "x_s")]
+        "x_s", "logits", "z_q", "z_s", "num_tiles")]
 
 
 _lib = None

@@ -2,11 +2,15 @@
 the kernel path).
 
 Rules restated from the pages:
-* Rate matching: the fraction of the GPUs given to attention follows
-  attention's fraction of the per-step cost, with at least one attention GPU
-  and the rest for the experts (AFD Disagg MoE notes page, case 2 on
-  capacity alignment).  The nearest integer is taken with ties to even, the
-  rounding of the language the page's example is written in.
+* Rate matching: the two pools should finish a step at the same rate, so
+  that neither waits for the other; a higher attention cost needs more
+  attention GPUs, a higher FFN cost more expert GPUs (AFD Disagg MoE notes
+  page, case 2 on capacity alignment).  Here that principle is applied
+  directly: with per-step costs t_a and t_f spread evenly over a pool, the
+  step period is the slower pool's, max(t_a / n_a, t_f / n_f), and n_a is the
+  integer in [1, N - 1] that minimises it (both pools must exist for the
+  layer to run).  Among splits with the same period the one nearest the
+  proportional share N t_a / (t_a + t_f) is taken, then the smaller n_a.
 * Micro-pipeline: with attention and FFN on separate pools the steady period
   is the longer stage plus the hand-over, max(t_a, t_f) + t_comm, against
   t_a + t_f when both run on the same GPUs (A/F 分离 page, 深入推导, 微流水).
@@ -23,15 +27,24 @@ from __future__ import annotations
 import json
 
 
+def step_period(attn_cost: float, ffn_cost: float, n_attn: int, n_ffn: int) -> float:
+    """Per-step period of two pools that each spread their stage evenly."""
+    return max(attn_cost / n_attn, ffn_cost / n_ffn)
+
+
 def split_gpus(attn_cost: float, ffn_cost: float, total_gpus: int):
-    """(attention GPUs, FFN GPUs) for stage costs measured in the same unit."""
+    """(attention GPUs, FFN GPUs) for stage costs measured in the same unit:
+    the split with the shortest step period (see the module notes)."""
     if total_gpus < 2:
         raise ValueError("need at least one GPU per pool")
     if attn_cost < 0 or ffn_cost < 0 or attn_cost + ffn_cost <= 0:
         raise ValueError("costs must be non-negative and not both zero")
-    share = attn_cost / (attn_cost + ffn_cost)
-    n_attn = round(total_gpus * share)  # nearest, ties to even
-    n_attn = min(max(n_attn, 1), total_gpus - 1)
+    share = total_gpus * attn_cost / (attn_cost + ffn_cost)
+
+    def rank(n):
+        return (step_period(attn_cost, ffn_cost, n, total_gpus - n), abs(n - share), n)
+
+    n_attn = min(range(1, total_gpus), key=rank)
     return n_attn, total_gpus - n_attn
 
 

@@ -150,24 +150,28 @@ int validate_weights(const afd_ffn_config *c, const afd_ffn_weights *w) {
   return AFD_OK;
 }
 
-// Record a profiling event pair around one stage's launches.
-hipEvent_t *prof_begin(afd_ffn_handle *h, int stage, hipStream_t s) {
-  if (!(h->prof_mask & (1u << stage))) return nullptr;
+// Record a profiling event pair around one stage's launches.  Returns the
+// pair's index in the pool (-1: stage not profiled); pairs may nest, so the
+// index, not a pointer into the growing pool, identifies the pair.
+int prof_begin(afd_ffn_handle *h, int stage, hipStream_t s) {
+  if (!(h->prof_mask & (1u << stage))) return -1;
   if (h->ev_used == h->ev_pool.size()) {
     StageEvents e;
-    if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess)
-      return nullptr;
+    if (hipEventCreate(&e.start) != hipSuccess) return -1;
+    if (hipEventCreate(&e.stop) != hipSuccess) {
+      hipEventDestroy(e.start);
+      return -1;
+    }
     h->ev_pool.push_back(e);
     h->ev_stage.push_back(stage);
   }
-  StageEvents &e = h->ev_pool[h->ev_used];
-  h->ev_stage[h->ev_used] = stage;
-  ++h->ev_used;
-  hipEventRecord(e.start, s);
-  return &e.stop;
+  const size_t i = h->ev_used++;
+  h->ev_stage[i] = stage;
+  hipEventRecord(h->ev_pool[i].start, s);
+  return static_cast<int>(i);
 }
-void prof_end(hipEvent_t *stop, hipStream_t s) {
-  if (stop) hipEventRecord(*stop, s);
+void prof_end(afd_ffn_handle *h, int i, hipStream_t s) {
+  if (i >= 0) hipEventRecord(h->ev_pool[static_cast<size_t>(i)].stop, s);
 }
 
 }  // namespace
@@ -288,11 +292,16 @@ static hipError_t launch_gemms(afd_ffn_handle *h, afd::GemmKind kind, const afd:
   a.tiles = h->tiles_big;
   a.num_tiles = h->num_big;
   a.tiles_ub = static_cast<int>(big_tiles_upper_bound(T, c.top_k, c.num_shared, plan.tiles.bm_big));
-  return afd::launch_gemm_prefill(kind, a, s);
+  const int ev = prof_begin(
+      h, kind == afd::GemmKind::GateUp ? AFD_STAGE_GATE_UP_BIG : AFD_STAGE_DOWN_BIG, s);
+  e = afd::launch_gemm_prefill(kind, a, s);
+  prof_end(h, ev, s);
+  return e;
 }
 
+// logits_out: optional [T, E] fp32 copy of the router logits (trace).
 static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
-                        hipStream_t s) {
+                        hipStream_t s, float *logits_out) {
   if (!h) return fail(AFD_ERR_INVALID_ARG, "handle is NULL");
   const afd_ffn_config &c = h->cfg;
   if (T < 0) return fail(AFD_ERR_INVALID_ARG, "T = %lld < 0", static_cast<long long>(T));
@@ -319,13 +328,13 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   const int hd = c.hidden;
   const int Tk = Ti * k;
   hipError_t e;
-  hipEvent_t *ev;
+  int ev;
 
   ev = prof_begin(h, AFD_STAGE_ROUTER, s);
   e = afd::launch_router(h->elem == 0, hidden, h->w.router_w,
                          c.has_router_bias ? h->w.router_b : nullptr, Ti, hd, E, k, h->logits,
-                         h->ids, h->topk_w, s);
-  prof_end(ev, s);
+                         h->ids, h->topk_w, logits_out, s);
+  prof_end(h, ev, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
 
   const afd::GemmPlan plan = afd::gemm_plan(h->elem, Ti, k, E);
@@ -333,7 +342,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   e = afd::launch_dispatch(h->ids, Ti, k, E, S, plan.tiles, h->counts, h->offsets, h->perm,
                            h->slot_row, h->tiles, h->num_tiles, h->tiles_big, h->num_big,
                            h->counters, 2, h->dispatch_scratch, s);
-  prof_end(ev, s);
+  prof_end(h, ev, s);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
 
   const uint8_t *A = static_cast<const uint8_t *>(hidden);
@@ -341,7 +350,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   if (h->elem == 2) {
     ev = prof_begin(h, AFD_STAGE_QUANT, s);
     e = afd::launch_quant_1x128(static_cast<const uint16_t *>(hidden), T, hd, h->xq, h->xs, s);
-    prof_end(ev, s);
+    prof_end(h, ev, s);
     if (e != hipSuccess) return hip_fail(e, "quantiser launch");
     A = h->xq;
     a_pitch = hd;
@@ -386,7 +395,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   }
   ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
   e = launch_gemms(h, afd::GemmKind::GateUp, plan, g, T, s);
-  prof_end(ev, s);
+  prof_end(h, ev, s);
   if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
   if (z_fp32) {
     ev = prof_begin(h, AFD_STAGE_QUANT, s);
@@ -401,7 +410,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
                                       h->z + static_cast<int64_t>(Tk) * h->zpitch, h->zpitch,
                                       h->zs + static_cast<int64_t>(Tk) * (h->zpitch / 128),
                                       h->zpitch / 128, s);
-    prof_end(ev, s);
+    prof_end(h, ev, s);
     if (e != hipSuccess) return hip_fail(e, "z quantiser launch");
   }
 
@@ -429,31 +438,32 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   d.work_counter = h->counters + 1;
   ev = prof_begin(h, AFD_STAGE_DOWN, s);
   e = launch_gemms(h, afd::GemmKind::Down, plan, d, T, s);
-  prof_end(ev, s);
+  prof_end(h, ev, s);
   if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
 
   ev = prof_begin(h, AFD_STAGE_COMBINE, s);
   e = afd::launch_combine(h->elem == 0, h->y, h->slot_row, h->topk_w, Ti, k, S, hd, out, s);
-  prof_end(ev, s);
+  prof_end(h, ev, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return AFD_OK;
 }
 
 int afd_ffn_forward(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
                     afd_stream_t stream) {
-  return forward_impl(h, hidden, out, T, static_cast<hipStream_t>(stream));
+  return forward_impl(h, hidden, out, T, static_cast<hipStream_t>(stream), nullptr);
 }
 
 int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out, int64_t T,
                            afd_stream_t stream, const afd_ffn_trace *tr) {
   if (!tr) return fail(AFD_ERR_INVALID_ARG, "trace is NULL");
-  if (h && T > 0 && (tr->x_q || tr->x_s) && h->elem != 2)
-    return fail(AFD_ERR_INVALID_ARG, "x_q / x_s are only produced in W8A8 mode");
-  int rc = forward_impl(h, hidden, out, T, static_cast<hipStream_t>(stream));
+  if (h && T > 0 && (tr->x_q || tr->x_s || tr->z_q || tr->z_s) && h->elem != 2)
+    return fail(AFD_ERR_INVALID_ARG, "x_q / x_s / z_q / z_s are only produced in W8A8 mode");
+  int rc = forward_impl(h, hidden, out, T, static_cast<hipStream_t>(stream), tr->logits);
   if (rc || T == 0) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const afd_ffn_config &c = h->cfg;
   const size_t tk = static_cast<size_t>(T) * c.top_k;
+  const size_t R = tk + static_cast<size_t>(c.num_shared) * T;
   struct Cp {
     void *dst;
     const void *src;
@@ -467,6 +477,10 @@ int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out, int
       {tr->slot_row, h->slot_row, tk * 4},
       {tr->x_q, h->xq, static_cast<size_t>(T) * c.hidden},
       {tr->x_s, h->xs, static_cast<size_t>(T) * (c.hidden / 128) * 4},
+      {tr->z_q, h->z, R * h->zpitch},
+      {tr->z_s, h->zs, R * (h->zpitch / 128) * 4},
+      {tr->num_tiles, h->num_tiles, 4},
+      {tr->num_tiles ? tr->num_tiles + 1 : nullptr, h->num_big, 4},
   };
   for (auto &cp : cps) {
     if (!cp.dst) continue;

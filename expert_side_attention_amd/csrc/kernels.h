@@ -22,11 +22,13 @@ constexpr int kMaxShared = 8;
 
 // Router GEMM + softmax + top-k + renormalisation.
 // f32: x, wr are fp32; else bf16.  bias may be null.  bf16 path scratch:
-// logits, router_logit_floats(T, h, E) floats.
+// logits, router_logit_floats(T, h, E) floats.  logits_out (may be null)
+// receives the [T, E] logits as ranked.
 int64_t router_logit_floats(int T, int h, int E);
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
-                         float *logits, int32_t *ids, float *w, hipStream_t s);
+                         float *logits, int32_t *ids, float *w, float *logits_out,
+                         hipStream_t s);
 
 // Row-tile lists of a forward: small tiles (bm_small rows) and, if
 // bm_big > 0, big tiles (bm_big rows) for groups of at least big_min rows.

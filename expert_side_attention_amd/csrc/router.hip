@@ -54,11 +54,13 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x)
 // Top-k over the logits of TM tokens (row pitch E, in LDS or global memory),
 // one wave per token at a time.  NC = candidates per lane (E <= 64 * NC).
 // A logit is the sum of `planes` partial values `plane` floats apart, added
-// in plane order, plus bias[e] when bias is not null.
+// in plane order, plus bias[e] when bias is not null.  With lout set, the
+// logits as ranked are also stored there ([T, E], for inspection).
 template <int TM, int NC, int WAVES = 4>
 __device__ void topk_rows(const float *sl, float *selv, int t0, int T,
                           int E, int k, int32_t *ids, float *wout, int planes = 1,
-                          int64_t plane = 0, const float *bias = nullptr) {
+                          int64_t plane = 0, const float *bias = nullptr,
+                          float *lout = nullptr) {
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   float *mysel = selv + wave * kMaxExperts;
@@ -83,7 +85,12 @@ __device__ void topk_rows(const float *sl, float *selv, int t0, int T,
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int e = lane + 64 * c;
-      key[c] = e < E ? topk_key(logit(e), e) : 0ull;
+      key[c] = 0ull;
+      if (e < E) {
+        const float v = logit(e);
+        key[c] = topk_key(v, e);
+        if (lout) lout[static_cast<int64_t>(t) * E + e] = v;
+      }
     }
     for (int j = 0; j < k; ++j) {
       unsigned long long best = 0;
@@ -219,11 +226,12 @@ template <int NC>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int T,
                                                    int E, int k, int32_t *__restrict__ ids,
                                                    float *__restrict__ wout, int planes,
-                                                   const float *__restrict__ bias) {
+                                                   const float *__restrict__ bias,
+                                                   float *__restrict__ lout) {
   __shared__ float selv[4 * kMaxExperts];
   const int t0 = blockIdx.x * 4;
   topk_rows<4, NC, 4>(logits + static_cast<int64_t>(t0) * E, selv, t0, T, E, k, ids, wout,
-                      planes, static_cast<int64_t>(T) * E, bias);
+                      planes, static_cast<int64_t>(T) * E, bias, lout);
 }
 
 // fp32 router for small layers: one (token, expert) dot product per thread.
@@ -231,7 +239,7 @@ template <int TM>
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float *__restrict__ X, const float *__restrict__ Wr,
     const float *__restrict__ bias, int T, int h, int E, int k,
-    int32_t *__restrict__ ids, float *__restrict__ wout) {
+    int32_t *__restrict__ ids, float *__restrict__ wout, float *__restrict__ lout) {
   __shared__ float sl[TM * kMaxExperts];
   __shared__ float selv[4 * kMaxExperts];
   const int t0 = blockIdx.x * TM;
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
     sl[tt * E + e] = a;
   }
   __syncthreads();
-  topk_rows<TM, kMaxExperts / 64>(sl, selv, t0, T, E, k, ids, wout);
+  topk_rows<TM, kMaxExperts / 64>(sl, selv, t0, T, E, k, ids, wout, 1, 0, nullptr, lout);
 }
 
 }  // namespace
@@ -260,22 +268,26 @@ int router_k_parts(int h, int E) { return E <= 64 && h % (4 * 256) == 0 ? 4 : 1;
 
 hipError_t launch_router(bool f32, const void *x, const void *wr,
                          const float *bias, int T, int h, int E, int k,
-                         float *logits, int32_t *ids, float *w, hipStream_t s) {
+                         float *logits, int32_t *ids, float *w, float *logits_out,
+                         hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (f32) {
     constexpr int TM = 16;
     router_f32_kernel<TM><<<(T + TM - 1) / TM, 256, 0, s>>>(
         static_cast<const float *>(x), static_cast<const float *>(wr), bias, T,
-        h, E, k, ids, w);
+        h, E, k, ids, w, logits_out);
     return hipGetLastError();
   }
   const uint16_t *X = static_cast<const uint16_t *>(x);
   const uint16_t *W = static_cast<const uint16_t *>(wr);
   const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
   auto topk = [&](int planes, const float *b) {
-    if (E <= 64) topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b);
-    else if (E <= 256) topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b);
-    else topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b);
+    if (E <= 64)
+      topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b, logits_out);
+    else if (E <= 256)
+      topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b, logits_out);
+    else
+      topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, w, planes, b, logits_out);
     return hipGetLastError();
   };
   if (T > kTiledRouterT) {

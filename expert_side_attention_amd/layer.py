@@ -128,7 +128,9 @@ class FfnLayer:
     def forward(self, hidden: torch.Tensor, out: torch.Tensor = None, stream=None,
                 trace: bool = False):
         """out [T, h] = layer(hidden [T, h]).  With trace=True also returns a
-        dict of the routing/dispatch intermediates of this call."""
+        dict of the routing/dispatch intermediates of this call (router
+        logits, ids, weights, dispatch, tile counts; W8A8: quantised input
+        and z)."""
         T = hidden.shape[0]
         _need(hidden, "hidden", self.act_dtype, (T, self.hidden), self.device)
         if out is None:
@@ -144,10 +146,16 @@ class FfnLayer:
               "counts": torch.empty((E,), dtype=torch.int32, device=d),
               "offsets": torch.empty((E + 1,), dtype=torch.int32, device=d),
               "perm": torch.empty((T * k,), dtype=torch.int32, device=d),
-              "slot_row": torch.empty((T, k), dtype=torch.int32, device=d)}
+              "slot_row": torch.empty((T, k), dtype=torch.int32, device=d),
+              "logits": torch.empty((T, E), dtype=torch.float32, device=d),
+              "num_tiles": torch.empty((2,), dtype=torch.int32, device=d)}
         if self.mode == "w8a8":
+            R = T * k + self.num_shared * T
+            Z = max(self.inter, self.shared_inter if self.num_shared else 0)
             tr["x_q"] = torch.empty((T, self.hidden), dtype=torch.uint8, device=d)
             tr["x_s"] = torch.empty((T, self.hidden // 128), dtype=torch.float32, device=d)
+            tr["z_q"] = torch.empty((R, Z), dtype=torch.uint8, device=d)
+            tr["z_s"] = torch.empty((R, Z // 128), dtype=torch.float32, device=d)
         ct = F.afd_ffn_trace(**{n: tr[n].data_ptr() for n in tr})
         F.afd_ffn_forward_traced(self._h, hidden.data_ptr(), out.data_ptr(), T, s, ct)
         return out, tr

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define AFD_FFN_ABI_VERSION 1u
+#define AFD_FFN_ABI_VERSION 2u
 
 typedef struct afd_ffn_handle afd_ffn_handle;
 typedef void *afd_stream_t; /* a hipStream_t */
@@ -71,7 +71,11 @@ typedef enum {
                              bf16 router                                    */
 } afd_mode;
 
-/* Layer configuration (host struct, copied by create()).
+/* Layer configuration (host struct, copied by create()).  One handle holds
+ * one layer; the FFN service is told per call which layer and micro-batch
+ * ("ubatch") it serves (vLLM AFD plugin page, "系統架構 / 1. Attention
+ * Service": data-parallel, ubatch, layer and graph state go to the FFN side),
+ * which here means: one handle per layer and per micro-batch stream.
  * Limits: 1 <= top_k <= num_experts <= 512; hidden, inter, shared_inter are
  * multiples of 128 (all modes); 0 <= num_shared <= 8 (shared_inter > 0 when
  * num_shared > 0); 1 <= max_tokens <= 1<<20 with max_tokens * top_k < 2^31. */
@@ -88,7 +92,9 @@ typedef struct {
   int32_t has_router_bias;/* 1: router_b is added to the logits              */
 } afd_ffn_config;
 
-/* Weight pointers (device, borrowed).  Element types by mode:
+/* Weight pointers (device, borrowed).  The experts are SwiGLU matrix
+ * products (A/F 分离 page, "为什么要拆"), W8A8 is the benchmark precision
+ * (vLLM AFD plugin page, "效能基準測試").  Element types by mode:
  *   router_w [E, h]           F32: fp32; BF16 and W8A8: bf16
  *   router_b [E]              fp32, only read when has_router_bias = 1
  *   gate_w, up_w [E, I, h]    F32: fp32; BF16: bf16; W8A8: E4M3 bytes
@@ -108,7 +114,9 @@ typedef struct {
 } afd_ffn_weights;
 
 /* Optional device buffers that forward_traced() fills with intermediate
- * results of the same call (any field may be NULL):
+ * results of the same call (any field may be NULL).  The routing step (vLLM
+ * AFD plugin page, "Attention-FFN 解耦的原理": routing computation) and the
+ * dispatch / combine of the expert path (A/F 分离 page, "机制"):
  *   topk_ids [T, k] int32   selected experts, slot order = logit descending,
  *                           index ascending
  *   topk_w   [T, k] fp32    renormalised routing weights
@@ -117,7 +125,17 @@ typedef struct {
  *   perm     [T*k] int32    token of each dispatched row (expert-contiguous,
  *                           tokens ascending inside an expert)
  *   slot_row [T, k] int32   dispatched row of each (token, slot)
- *   x_q [T, h] uint8, x_s [T, h/128] fp32   W8A8 only: quantised input    */
+ *   x_q [T, h] uint8, x_s [T, h/128] fp32   W8A8 only: quantised input
+ *   logits   [T, E] fp32    the router logits the top-k ranked (fp32
+ *                           accumulation of the products, plus the bias)
+ *   z_q [R, Z] uint8, z_s [R, Z/128] fp32   W8A8 only: the E4M3 SwiGLU
+ *                           output fed to the down product and its 1x128
+ *                           scales, R = T*k + S*T dispatched rows (routed
+ *                           rows in expert order, then row T*k + s*T + t for
+ *                           shared expert s on token t), Z = max(I, I_s);
+ *                           shared rows hold I_s valid columns
+ *   num_tiles [2] int32     row tiles of the expert GEMMs: weight-streaming
+ *                           tiles, then compute-bound 256-row tiles          */
 typedef struct {
   int32_t *topk_ids;
   float *topk_w;
@@ -127,35 +145,63 @@ typedef struct {
   int32_t *slot_row;
   uint8_t *x_q;
   float *x_s;
+  float *logits;
+  uint8_t *z_q;
+  float *z_s;
+  int32_t *num_tiles;
 } afd_ffn_trace;
 
 /* Create a layer handle: validates cfg and w, allocates the per-handle
  * workspace for max_tokens tokens (hipMalloc, on the current device).
+ * The configuration is checked up front and misuse is refused at once
+ * rather than degraded silently (plugin article "Separar Attention de FFN",
+ * "Con qué te vas a tropezar" and "Ejecutarlo en una sola máquina").
+ * cfg and w are read during the call only; *out receives the handle (NULL
+ * on error), owned by the caller until afd_ffn_destroy().  Errors:
+ * AFD_ERR_INVALID_ARG (bad or NULL argument, see the limits above),
+ * AFD_ERR_UNSUPPORTED, AFD_ERR_OUT_OF_MEMORY.
  * One handle runs one forward at a time; use one handle per micro-batch
  * stream (handles may share the same weights).                           */
 int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
                    afd_ffn_handle **out);
 
-/* out[T, h] = MoE-FFN(hidden[T, h]).  hidden/out: fp32 in F32 mode, bf16
- * otherwise, 16-byte aligned; they must not overlap.  0 <= T <= max_tokens
- * (T = 0 is a no-op).  Asynchronous on `stream`; the handle's workspace is in use until
- * the enqueued work completes.                                            */
+/* out[T, h] = MoE-FFN(hidden[T, h]): the FFN service's step on the hidden
+ * states it receives, whose result goes back to the attention side (vLLM
+ * AFD plugin page, "系統架構 / 2. FFN Service"; capturable into a graph as
+ * the sync connectors' decode graphs need: "Connector 與後端支援矩陣").
+ * hidden/out: device arrays [T, h], row-major, fp32 in F32 mode, bf16
+ * otherwise, 16-byte aligned, owned by the caller; they must not overlap.
+ * 0 <= T <= max_tokens (T = 0 is a no-op).  Errors: AFD_ERR_INVALID_ARG
+ * (NULL, misaligned, overlapping, T < 0, wrong current device),
+ * AFD_ERR_CAPACITY (T > max_tokens), AFD_ERR_HIP (launch failure).
+ * Asynchronous on `stream`; the handle's workspace is in use until the
+ * enqueued work completes.                                                */
 int afd_ffn_forward(afd_ffn_handle *h, const void *hidden, void *out,
                     int64_t T, afd_stream_t stream);
 
-/* forward() plus copies of intermediates into `trace` (see afd_ffn_trace). */
+/* forward() plus the intermediates of the same call written to `trace`
+ * (see afd_ffn_trace; the routing, dispatch and W8A8 steps named there).
+ * Trace buffers are device memory owned by the caller, sized for this T.
+ * Errors: those of forward(), and AFD_ERR_INVALID_ARG for a NULL trace or
+ * for x_q / x_s / z_q / z_s outside W8A8 mode.                            */
 int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out,
                            int64_t T, afd_stream_t stream,
                            const afd_ffn_trace *trace);
 
 /* Free the workspace and the handle (waits for the device to finish work
- * that uses it).  NULL is ignored.                                        */
+ * that uses it).  The counterpart of create(): the FFN service's state for
+ * one layer (vLLM AFD plugin page, "系統架構 / 2. FFN Service").  The
+ * borrowed weights are not touched.  NULL is ignored.                     */
 void afd_ffn_destroy(afd_ffn_handle *h);
 
-/* FP8 E4M3 activation quantiser: one scale per row per 128 columns.
+/* FP8 E4M3 activation quantiser of the W8A8 layer (vLLM AFD plugin page,
+ * "效能基準測試": W8A8): one scale per row per 128 columns.
  * x [rows, cols] bf16 -> q [rows, cols] E4M3 bytes, s [rows, cols/128] fp32,
  * s = fl32(amax/448) (1 if that is 0), q = RNE-saturating E4M3 of
- * fl32(x/s).  cols % 128 == 0; x and q 16-byte aligned, s 4-byte.       */
+ * fl32(x/s).  Device arrays owned by the caller, row-major, contiguous;
+ * x and q 16-byte aligned, s 4-byte.  Errors: NULL or misaligned pointer,
+ * rows < 0 or cols not a positive multiple of 128 -> AFD_ERR_INVALID_ARG;
+ * rows = 0 is a no-op.                                                    */
 int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols,
                         uint8_t *q, float *s, afd_stream_t stream);
 
@@ -169,29 +215,43 @@ int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols,
 int afd_quant_fp8_1x128_f32(const float *x, int64_t rows, int64_t cols,
                             uint8_t *q, float *s, afd_stream_t stream);
 
-/* FP8 E4M3 weight quantiser: one scale per 128x128 block, same rounding.
- * w [rows, cols] bf16 -> q [rows, cols], s [rows/128, cols/128].
- * rows % 128 == 0, cols % 128 == 0.  A stack [E, N, K] is rows = E*N.
- * w and q 16-byte aligned, s 4-byte.                                      */
+/* FP8 E4M3 weight quantiser of the W8A8 layer (vLLM AFD plugin page,
+ * "效能基準測試"): one scale per 128x128 block, same rounding.
+ * w [rows, cols] bf16 -> q [rows, cols], s [rows/128, cols/128], device
+ * arrays owned by the caller.  rows % 128 == 0, cols % 128 == 0.  A stack
+ * [E, N, K] is rows = E*N.  w and q 16-byte aligned, s 4-byte.  Errors:
+ * NULL, misaligned or non-multiple-of-128 -> AFD_ERR_INVALID_ARG.         */
 int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols,
                           uint8_t *q, float *s, afd_stream_t stream);
 
-/* Kernel-level timing: with stage_mask != 0, subsequent forwards record HIP
- * events (on the forward's stream) around the launches of the selected
- * stages; afd_ffn_profile_read() waits for them and returns the summed
- * milliseconds and launch counts per stage, then resets.  Stage bits:     */
+/* Kernel-level timing, for finding where the layer's time goes (LLM 推理提速
+ * page, "一个在啃带宽，一个在吃算力": the bound of each side is found by
+ * profiling).  With stage_mask != 0, subsequent forwards record HIP events
+ * (on the forward's stream) around the launches of the selected stages;
+ * afd_ffn_profile_read() waits for them and returns the summed milliseconds
+ * and launch counts per stage (host arrays of AFD_STAGE_COUNT owned by the
+ * caller), then resets.  Errors: NULL handle or arrays, unknown bits ->
+ * AFD_ERR_INVALID_ARG; a failed event -> AFD_ERR_HIP.  The compute-bound
+ * launches of the gate/up and down stages (256-row tiles) are also timed
+ * on their own under AFD_STAGE_GATE_UP_BIG and AFD_STAGE_DOWN_BIG.  Stage
+ * bits:                                                                    */
 #define AFD_STAGE_ROUTER   0
 #define AFD_STAGE_DISPATCH 1
 #define AFD_STAGE_QUANT    2
 #define AFD_STAGE_GATE_UP  3
 #define AFD_STAGE_DOWN     4
 #define AFD_STAGE_COMBINE  5
-#define AFD_STAGE_COUNT    6
+#define AFD_STAGE_GATE_UP_BIG 6
+#define AFD_STAGE_DOWN_BIG 7
+#define AFD_STAGE_COUNT    8
 int afd_ffn_profile_enable(afd_ffn_handle *h, uint32_t stage_mask);
 int afd_ffn_profile_read(afd_ffn_handle *h, double *ms /*[AFD_STAGE_COUNT]*/,
                          int64_t *launches /*[AFD_STAGE_COUNT]*/);
 
-/* Thread-local description of the last error returned on this thread.    */
+/* Thread-local description of the last error returned on this thread (the
+ * message that comes with a refused call: plugin article "Separar Attention
+ * de FFN", "Ejecutarlo en una sola máquina").  Owned by the library, valid
+ * until the next call on the same thread; "" if none.                     */
 const char *afd_ffn_last_error(void);
 
 #ifdef __cplusplus

@@ -12,6 +12,17 @@ fp32 sums are exact and the lowest-index rule must hold bit for bit.
 Dispatch: given the GPU's ids, counts/offsets/perm/slot_row must equal the
 oracle's dispatch of those ids bit for bit.
 
+Router logits (traced): the GPU's fp32 logits must lie within the rigorous
+bound beta of the oracle's, and within a realistic one: rounding errors of a
+sum of h terms grow like a random walk, so 4 sqrt(h + 2) 2^-24 (sum_i |x_i
+w_ei| + |b_e|) leaves a wide margin.  Given its own logits, the GPU's
+selection must be bit-exact (the top-k by (logit desc, index asc)) and its
+weights must be the renormalised softmax of those logits up to the fp32
+rounding of exp, sum and divide.
+
+W8A8 z (traced): the E4M3 codes and 1x128 scales the gate/up step feeds to
+the down product, against the oracle's z of the same rows (see check_w8a8_z).
+
 Outputs: rel-L2 <= 5e-3 and max-abs <= 1e-2 max|ref| (fp32, bf16); rel-L2 <=
 2e-2 for W8A8.  Tokens whose selected experts differ from the oracle's
 (near ties) are excluded from the output comparison and counted.
@@ -29,11 +40,132 @@ def decode_store(a, mode):
     return np.asarray(a, np.float32).astype(np.float64) if mode == "f32" else O.bf16_to_f64(a)
 
 
-def routing_slack(x64, wr64, b, h):
+U32 = 2.0 ** -24
+
+
+def logit_abs_sums(x64, wr64, b):
+    """sum_i |x_i w_ei| (+ |b_e|) for every (token, expert)."""
     s = np.abs(x64) @ np.abs(wr64).T
     if b is not None:
         s = s + np.abs(np.asarray(b, np.float64))[None, :]
-    return (h + 2) * 2.0 ** -24 * s
+    return s
+
+
+def routing_slack(x64, wr64, b, h):
+    return (h + 2) * U32 * logit_abs_sums(x64, wr64, b)
+
+
+def check_gpu_logits(gpu_logits, ref_logits, sums, h):
+    """GPU fp32 logits vs the oracle's fp64 logits; returns the largest error
+    as a fraction of the rigorous and of the realistic bound."""
+    g = np.asarray(gpu_logits, np.float64)
+    err = np.abs(g - ref_logits)
+    rigorous = (h + 2) * U32 * sums
+    realistic = 4.0 * np.sqrt(h + 2) * U32 * sums
+    assert np.all(err <= rigorous), f"logit error {err.max():.3e} beyond the worst-case bound"
+    worst = np.unravel_index(np.argmax(err / realistic), err.shape)
+    assert np.all(err <= realistic), (f"logit error {err[worst]:.3e} at {worst} beyond "
+                                      f"{realistic[worst]:.3e}")
+    return float(np.max(err / rigorous)), float(np.max(err / realistic))
+
+
+def check_selection_on_gpu_logits(gpu_logits, gpu_ids, k):
+    """Bit-exact: the ids are the top-k of the GPU's own logits, slots by
+    (logit descending, index ascending)."""
+    want = O.select_topk(np.asarray(gpu_logits, np.float64), k)
+    bad = np.nonzero(np.any(np.asarray(gpu_ids) != want, axis=1))[0]
+    assert bad.size == 0, f"tokens {bad[:10]} do not take the top-k of their own logits"
+
+
+def check_weights_on_gpu_logits(gpu_w, gpu_logits, gpu_ids):
+    """w_j = exp(l_j - m) / sum_j' exp(l_j' - m) of the GPU's own logits (m =
+    max over all experts), computed in fp64.  fp32 error budget per weight:
+    l_j - m rounds with relative error u, i.e. |l_j - m| u in the exponent;
+    expf within 2 ulp; the sum of k terms; the divide: |dw_j| <= w_j 2 u
+    (|l_j - m| + max_j' |l_j' - m| + k + 6), u = 2^-24.  Returns the largest
+    relative error."""
+    l = np.asarray(gpu_logits, np.float64)
+    ids = np.asarray(gpu_ids, np.int64)
+    k = ids.shape[1]
+    m = l.max(axis=1, keepdims=True)
+    d = m - np.take_along_axis(l, ids, 1)
+    ex = np.exp(-d)
+    ref = ex / ex.sum(axis=1, keepdims=True)
+    bound = ref * 2 * U32 * (d + d.max(axis=1, keepdims=True) + k + 6)
+    err = np.abs(np.asarray(gpu_w, np.float64) - ref)
+    assert np.all(err <= bound), f"weights off by {np.max(err / ref):.3e} relative"
+    return float(np.max(err / ref))
+
+
+def _e4m3_half_spacing(v):
+    """Half the E4M3 grid spacing at |v| (v already divided by the scale)."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.where(a < 2.0 ** -6, 2.0 ** -10, 2.0 ** (e - 4))
+
+
+def check_w8a8_z(orc, x_store, tr, groups=None):
+    """The E4M3 z and 1x128 scales of dispatched rows (traced z_q / z_s) vs
+    the oracle's z of the same (token, expert) pairs, in fp64 from the same
+    quantised input and weights.  Per element, the GPU's fp32 accumulation
+    may differ from fp64 by dz <= 1.1 |u| dg + |silu(g)| du + 4 u |z| with
+    dg, du <= 4 sqrt(h) u sum_i |x_i w_i| (the realistic bound above).
+    Checks: each group's scale within (max dz) / 448 + 2 u s of fl32(amax /
+    448); each group's largest code decodes to +-448; every dequantised
+    element within the E4M3 rounding of the GPU's z (half a grid step at
+    z / s) of the oracle's z, plus dz; and at least 99% of the codes equal
+    the oracle's own encoding.  groups: the routed experts to check (default
+    all); shared rows are always checked.  Returns (rows checked, fraction
+    of equal codes)."""
+    s = orc.shape
+    xin, _ = orc.expert_input(x_store)
+    T, k = xin.shape[0], s.k
+    Tk = T * k
+    offsets = np.asarray(tr["offsets"], np.int64)
+    perm = np.asarray(tr["perm"], np.int64)
+    zq, zs = np.asarray(tr["z_q"]), np.asarray(tr["z_s"])
+    todo = []
+    for e in (range(s.E) if groups is None else groups):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if rows.size:
+            todo.append((orc.src.expert(e), rows, perm[rows], s.I))
+    for j in range(s.S):
+        todo.append((orc.src.shared(j), Tk + j * T + np.arange(T), np.arange(T), s.Is))
+    c = 4.0 * np.sqrt(s.h) * U32
+    n_rows = n_eq = n_el = 0
+    for mats, rows, toks, N in todo:
+        G, U, _ = orc._weights(mats)
+        xr = xin[toks]
+        g, u = xr @ G.T, xr @ U.T
+        sg, su = np.abs(xr) @ np.abs(G).T, np.abs(xr) @ np.abs(U).T
+        z = O.silu(g) * u
+        dz = 1.1 * np.abs(u) * c * sg + np.abs(O.silu(g)) * c * su + 4 * U32 * np.abs(z)
+        z32 = z.astype(np.float32).astype(np.float64)
+        q = zq[rows, :N]
+        sc = zs[rows, :N // 128].astype(np.float64)
+        R = len(rows)
+        zg = z32.reshape(R, N // 128, 128)
+        amax = np.abs(zg).max(axis=2)
+        s_ref = (amax / 448.0).astype(np.float32).astype(np.float64)
+        s_ref = np.where((amax == 0) | (s_ref == 0), 1.0, s_ref)
+        ds = dz.reshape(R, N // 128, 128).max(axis=2) / 448.0 + 2 * U32 * s_ref
+        assert np.all(np.abs(sc - s_ref) <= ds), \
+            f"z scales off by {np.max(np.abs(sc - s_ref) / s_ref):.3e} relative"
+        vals = O.e4m3_decode(q).reshape(R, N // 128, 128)
+        nz = np.abs(vals).max(axis=2) > 0
+        assert np.all(np.abs(vals).max(axis=2)[nz] == 448.0), "a group's largest code is not 448"
+        deq = vals * sc[..., None]
+        tol = (_e4m3_half_spacing(deq / sc[..., None]) * sc[..., None] * (1 + 1e-6)
+               + 2 * dz.reshape(R, N // 128, 128))
+        err = np.abs(deq - zg)
+        assert np.all(err <= tol), f"dequantised z off by {np.max(err - tol):.3e} beyond its bound"
+        own = O.e4m3_encode((zg / s_ref[..., None]).astype(np.float32)).reshape(R, N)
+        n_eq += int(np.sum(own == q))
+        n_el += q.size
+        n_rows += R
+    frac = n_eq / max(n_el, 1)
+    assert frac >= 0.99, f"only {frac:.4f} of the z codes equal the oracle's"
+    return n_rows, frac
 
 
 def check_routing(logits, beta, gpu_ids, k):

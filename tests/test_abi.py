@@ -41,10 +41,11 @@ def test_struct_layout_matches_c_compiler(tmp_path):
 #include <stddef.h>
 #include "afd_ffn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(afd_ffn_config),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(afd_ffn_config),
          sizeof(afd_ffn_weights), sizeof(afd_ffn_trace),
          offsetof(afd_ffn_config, max_tokens), offsetof(afd_ffn_weights, down_s),
-         offsetof(afd_ffn_weights, sh_down_s), offsetof(afd_ffn_trace, x_s));
+         offsetof(afd_ffn_weights, sh_down_s), offsetof(afd_ffn_trace, x_s),
+         offsetof(afd_ffn_trace, num_tiles));
   return 0;
 }
 """)
@@ -56,7 +57,7 @@ int main(void) {
     want = [ctypes.sizeof(F.afd_ffn_config), ctypes.sizeof(F.afd_ffn_weights),
             ctypes.sizeof(F.afd_ffn_trace), F.afd_ffn_config.max_tokens.offset,
             F.afd_ffn_weights.down_s.offset, F.afd_ffn_weights.sh_down_s.offset,
-            F.afd_ffn_trace.x_s.offset]
+            F.afd_ffn_trace.x_s.offset, F.afd_ffn_trace.num_tiles.offset]
     assert got == want
 
 

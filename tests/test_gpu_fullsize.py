@@ -13,8 +13,9 @@ import torch
 from afd_inputs import CONFIGS, SyntheticLayer
 from oracle import afd_oracle as O
 
-from parity import (check_dispatch, check_outputs, check_routing, check_weights, decode_store,
-                    routing_slack)
+from parity import (check_dispatch, check_gpu_logits, check_outputs, check_routing,
+                    check_selection_on_gpu_logits, check_w8a8_z, check_weights,
+                    check_weights_on_gpu_logits, decode_store, logit_abs_sums)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -65,15 +66,25 @@ def check_full(name, microbatches=1, n_sample=12):
 
     orc = O.OracleFFN(syn, threads=16)
     logits, ids, w = orc.route(x)
-    beta = routing_slack(decode_store(x, s.mode), orc._wr, orc._b, s.h)
+    sums = logit_abs_sums(decode_store(x, s.mode), orc._wr, orc._b)
+    beta = (s.h + 2) * 2.0 ** -24 * sums
     gpu_ids = np.concatenate([tr["topk_ids"] for tr in trs])
+    gpu_logits = np.concatenate([tr["logits"] for tr in trs])
+    lr, lq = check_gpu_logits(gpu_logits, logits, sums, s.h)
+    check_selection_on_gpu_logits(gpu_logits, gpu_ids, s.k)
+    wrel = check_weights_on_gpu_logits(np.concatenate([tr["topk_w"] for tr in trs]),
+                                       gpu_logits, gpu_ids)
+    print(f"[fullsize] {name}: logits within {lr:.2e} of the worst-case bound, {lq:.2e} of "
+          f"the realistic one; weights {wrel:.2e} relative to the GPU logits' softmax",
+          flush=True)
     differ = check_routing(logits, beta, gpu_ids, s.k)
     print(f"[fullsize] {name}: {int(differ.sum())} near-tie tokens of {T}", flush=True)
     assert differ.mean() <= 0.01
     same = ~differ
     gpu_w = np.concatenate([tr["topk_w"] for tr in trs])
     ratio = check_weights(gpu_w, w, beta, gpu_ids, same)
-    print(f"[fullsize] {name}: routing weights within {ratio:.2f} of their bound", flush=True)
+    print(f"[fullsize] {name}: routing weights within {ratio:.2e} of their worst-case bound",
+          flush=True)
     for tr in trs:
         check_dispatch(tr, s.E)
     if s.mode == "w8a8":
@@ -88,6 +99,13 @@ def check_full(name, microbatches=1, n_sample=12):
                 rq, rs = O.quantize_128x128(O.bf16_to_f64(m).astype(np.float32))
                 assert np.array_equal(wq[e].cpu().numpy(), rq)
                 assert np.array_equal(ws[e].cpu().numpy(), rs)
+        # E4M3 z of every row of three experts and of the shared expert
+        for i, tr in enumerate(trs):
+            xm = x[i * mbT:(i + 1) * mbT]
+            busy = np.argsort(-tr["counts"], kind="stable")[:3]
+            rows, frac = check_w8a8_z(orc, xm, tr, groups=[int(e) for e in busy])
+            print(f"[fullsize] {name}: W8A8 z of {rows} rows, {frac:.5f} of the codes equal "
+                  f"the oracle's", flush=True)
     tokens = [t for t in _sample(T, n_sample) if same[t]]
     print(f"[fullsize] {name}: oracle outputs of tokens {tokens}", flush=True)
     ref = orc.forward(x, tokens=tokens)

@@ -9,8 +9,9 @@ import torch
 from afd_inputs import CONFIGS, LayerShape, SyntheticLayer, f32_to_bf16_bits, tie_case
 from oracle import afd_oracle as O
 
-from parity import (TOL, check_dispatch, check_outputs, check_routing, check_weights,
-                    decode_store, routing_slack)
+from parity import (TOL, check_dispatch, check_gpu_logits, check_outputs, check_routing,
+                    check_selection_on_gpu_logits, check_w8a8_z, check_weights,
+                    check_weights_on_gpu_logits, decode_store, logit_abs_sums)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,11 @@ def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False):
     orc = O.OracleFFN(syn, threads=threads)
     ref = orc.forward(x)
     x64 = decode_store(x, s.mode)
-    beta = routing_slack(x64, orc._wr, orc._b, s.h)
+    sums = logit_abs_sums(x64, orc._wr, orc._b)
+    beta = (s.h + 2) * 2.0 ** -24 * sums
+    lr, lq = check_gpu_logits(tr["logits"], ref["logits"], sums, s.h)
+    check_selection_on_gpu_logits(tr["logits"], tr["topk_ids"], s.k)
+    wrel = check_weights_on_gpu_logits(tr["topk_w"], tr["logits"], tr["topk_ids"])
     differ = check_routing(ref["logits"], beta, tr["topk_ids"], s.k)
     if expect_exact_routing:
         assert not differ.any()
@@ -51,9 +56,14 @@ def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False):
     check_dispatch(tr, s.E)
     same = ~differ
     check_weights(tr["topk_w"], ref["w"], beta, tr["topk_ids"], same)
+    print(f"[parity] logits: max error {lr:.2e} of the worst-case bound, {lq:.2e} of the "
+          f"realistic one; weights {wrel:.2e} relative to the GPU logits' softmax", flush=True)
     if s.mode == "w8a8":
         assert np.array_equal(tr["x_q"], ref["x_q"])
         assert np.array_equal(tr["x_s"], ref["x_s"])
+        rows, frac = check_w8a8_z(orc, x, tr)
+        print(f"[parity] W8A8 z of {rows} rows: {frac:.5f} of the codes equal the oracle's",
+              flush=True)
     rel, mabs = check_outputs(out, ref["out"], s.mode, keep=same)
     print(f"[parity] rel-L2 {rel:.3e} max-abs/max {mabs:.3e} "
           f"near-tie tokens {int(differ.sum())}", flush=True)

@@ -1,14 +1,24 @@
 """The attention/FFN micro-pipeline harness: every placement of the
 ping-pong schedule (co-located on one stream, overlapped on two streams,
 split over CU-masked streams) yields the hidden states of the plain loop
-over layers and micro-batches, bit for bit."""
+over layers and micro-batches, bit for bit; and in that loop the FFN
+service's output of every layer and micro-batch matches the fp64 oracle on
+the input that layer received."""
+import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
 
 from afd_inputs import LayerShape, SyntheticLayer  # noqa: E402
+from oracle import afd_oracle as O  # noqa: E402
+
+from parity import check_outputs, check_routing, decode_store, routing_slack  # noqa: E402
 
 pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
 def test_pipeline_placements_agree():
@@ -29,10 +39,22 @@ def test_pipeline_placements_agree():
 
     hb = [xi.clone() for xi in xs]
     ab = [torch.empty_like(xi) for xi in xs]
-    for _ in range(layers):
+    orc = O.OracleFFN(syn, threads=8)
+    for layer in range(layers):
         for m in range(M):
             attn[m].forward(hb[m], ab[m])
-            ffns[m].forward(ab[m], out=hb[m])
+            _, tr = ffns[m].forward(ab[m], out=hb[m], trace=True)
+            torch.cuda.synchronize()
+            # the FFN service's step of this layer vs the oracle on its input
+            a = _bits(ab[m])
+            ref = orc.forward(a)
+            beta = routing_slack(decode_store(a, "bf16"), orc._wr, orc._b, shape.h)
+            differ = check_routing(ref["logits"], beta, tr["topk_ids"].cpu().numpy(), shape.k)
+            assert differ.mean() <= 0.01
+            rel, mabs = check_outputs(O.bf16_to_f64(_bits(hb[m])), ref["out"], "bf16",
+                                      keep=~differ)
+            print(f"[pipeline] layer {layer} micro-batch {m}: FFN vs oracle rel-L2 {rel:.3e}",
+                  flush=True)
     torch.cuda.synchronize()
     for m in range(M):
         assert torch.isfinite(hb[m].float()).all()
