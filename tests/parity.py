@@ -107,16 +107,23 @@ def _e4m3_half_spacing(v):
 def check_w8a8_z(orc, x_store, tr, groups=None):
     """The E4M3 z and 1x128 scales of dispatched rows (traced z_q / z_s) vs
     the oracle's z of the same (token, expert) pairs, in fp64 from the same
-    quantised input and weights.  Per element, the GPU's fp32 accumulation
-    may differ from fp64 by dz <= 1.1 |u| dg + |silu(g)| du + 4 u |z| with
-    dg, du <= 4 sqrt(h) u sum_i |x_i w_i| (the realistic bound above).
+    quantised input and weights.  Per element, the GPU's accumulation may
+    differ from fp64 by dz <= 1.1 |u| dg + |silu(g)| du + 4 u |z| with dg, du
+    <= c sum_i |x_i w_i|.  The gfx950 fp8 MFMAs do not sum their 32 products
+    in IEEE fp32: product bits more than about 13 below the largest product
+    of one instruction are dropped (measured with a small in-bounds probe of
+    the 16x16x32 fp8 instruction: 448 + 127 * 2^-9 sums to 448.234375).
+    Those truncations add like a random walk over the h / 32 instructions of
+    a dot product whose largest products are a few times the mean, so c =
+    2^-13 sqrt(32) / sqrt(h / 32) = 2^-8 / sqrt(h), or the fp32 random-walk
+    bound 4 sqrt(h) 2^-24 where that is larger.
     Checks: each group's scale within (max dz) / 448 + 2 u s of fl32(amax /
     448); each group's largest code decodes to +-448; every dequantised
     element within the E4M3 rounding of the GPU's z (half a grid step at
     z / s) of the oracle's z, plus dz; and at least 99% of the codes equal
     the oracle's own encoding.  groups: the routed experts to check (default
     all); shared rows are always checked.  Returns (rows checked, fraction
-    of equal codes)."""
+    of equal codes, largest scale deviation as a fraction of its bound)."""
     s = orc.shape
     xin, _ = orc.expert_input(x_store)
     T, k = xin.shape[0], s.k
@@ -131,8 +138,9 @@ def check_w8a8_z(orc, x_store, tr, groups=None):
             todo.append((orc.src.expert(e), rows, perm[rows], s.I))
     for j in range(s.S):
         todo.append((orc.src.shared(j), Tk + j * T + np.arange(T), np.arange(T), s.Is))
-    c = 4.0 * np.sqrt(s.h) * U32
+    c = max(4.0 * np.sqrt(s.h) * U32, 2.0 ** -8 / np.sqrt(s.h))
     n_rows = n_eq = n_el = 0
+    worst = 0.0
     for mats, rows, toks, N in todo:
         G, U, _ = orc._weights(mats)
         xr = xin[toks]
@@ -149,6 +157,7 @@ def check_w8a8_z(orc, x_store, tr, groups=None):
         s_ref = (amax / 448.0).astype(np.float32).astype(np.float64)
         s_ref = np.where((amax == 0) | (s_ref == 0), 1.0, s_ref)
         ds = dz.reshape(R, N // 128, 128).max(axis=2) / 448.0 + 2 * U32 * s_ref
+        worst = max(worst, float(np.max(np.abs(sc - s_ref) / ds)))
         assert np.all(np.abs(sc - s_ref) <= ds), \
             f"z scales off by {np.max(np.abs(sc - s_ref) / s_ref):.3e} relative"
         vals = O.e4m3_decode(q).reshape(R, N // 128, 128)
@@ -165,7 +174,7 @@ def check_w8a8_z(orc, x_store, tr, groups=None):
         n_rows += R
     frac = n_eq / max(n_el, 1)
     assert frac >= 0.99, f"only {frac:.4f} of the z codes equal the oracle's"
-    return n_rows, frac
+    return n_rows, frac, worst
 
 
 def check_routing(logits, beta, gpu_ids, k):

@@ -103,9 +103,9 @@ def check_full(name, microbatches=1, n_sample=12):
         for i, tr in enumerate(trs):
             xm = x[i * mbT:(i + 1) * mbT]
             busy = np.argsort(-tr["counts"], kind="stable")[:3]
-            rows, frac = check_w8a8_z(orc, xm, tr, groups=[int(e) for e in busy])
+            rows, frac, worst = check_w8a8_z(orc, xm, tr, groups=[int(e) for e in busy])
             print(f"[fullsize] {name}: W8A8 z of {rows} rows, {frac:.5f} of the codes equal "
-                  f"the oracle's", flush=True)
+                  f"the oracle's, scales within {worst:.2f} of their bound", flush=True)
     tokens = [t for t in _sample(T, n_sample) if same[t]]
     print(f"[fullsize] {name}: oracle outputs of tokens {tokens}", flush=True)
     ref = orc.forward(x, tokens=tokens)

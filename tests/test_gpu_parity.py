@@ -61,9 +61,9 @@ def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False):
     if s.mode == "w8a8":
         assert np.array_equal(tr["x_q"], ref["x_q"])
         assert np.array_equal(tr["x_s"], ref["x_s"])
-        rows, frac = check_w8a8_z(orc, x, tr)
-        print(f"[parity] W8A8 z of {rows} rows: {frac:.5f} of the codes equal the oracle's",
-              flush=True)
+        rows, frac, worst = check_w8a8_z(orc, x, tr)
+        print(f"[parity] W8A8 z of {rows} rows: {frac:.5f} of the codes equal the oracle's, "
+              f"scales within {worst:.2f} of their bound", flush=True)
     rel, mabs = check_outputs(out, ref["out"], s.mode, keep=same)
     print(f"[parity] rel-L2 {rel:.3e} max-abs/max {mabs:.3e} "
           f"near-tie tokens {int(differ.sum())}", flush=True)

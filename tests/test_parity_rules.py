@@ -99,7 +99,7 @@ def test_w8a8_z_rule_accepts_fp32_and_rejects_mistakes():
     syn = SyntheticLayer(shape, seed=4)
     orc = O.OracleFFN(syn)
     x, tr = _z_trace_fp32(syn, orc)
-    rows, frac = check_w8a8_z(orc, x, tr)
+    rows, frac, _ = check_w8a8_z(orc, x, tr)
     assert rows == 48 * 2 + 48 and frac > 0.999
 
     def wrong_axis(z):                            # groups of 128 consecutive rows
