@@ -19,6 +19,7 @@ AFD_FFN_ABI_VERSION = 2
 AFD_OK, AFD_ERR_INVALID_ARG, AFD_ERR_UNSUPPORTED = 0, 1, 2
 AFD_ERR_CAPACITY, AFD_ERR_OUT_OF_MEMORY, AFD_ERR_HIP = 3, 4, 5
 AFD_MODE_F32, AFD_MODE_BF16, AFD_MODE_W8A8_E4M3 = 0, 1, 2
+AFD_FFN_STATIC_SCRATCH_BYTES = 128 << 20
 STAGES = ("router", "dispatch", "quant", "gate_up", "down", "combine", "gate_up_big",
           "down_big")
 STAGE_INDEX = {n: i for i, n in enumerate(STAGES)}
@@ -75,6 +76,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "afd_ffn_forward_traced": (ctypes.c_int, [P, P, P, I64, P,
                                                   ctypes.POINTER(afd_ffn_trace)]),
         "afd_ffn_destroy": (None, [P]),
+        "afd_ffn_forward_static": (ctypes.c_int, [ctypes.POINTER(afd_ffn_config),
+                                                  ctypes.POINTER(afd_ffn_weights),
+                                                  P, P, I64, P]),
         "afd_quant_fp8_1x128": (ctypes.c_int, [P, I64, I64, P, P, P]),
         "afd_quant_fp8_128x128": (ctypes.c_int, [P, I64, I64, P, P, P]),
         "afd_quant_fp8_1x128_f32": (ctypes.c_int, [P, I64, I64, P, P, P]),
@@ -118,6 +122,12 @@ def afd_ffn_forward_traced(h, hidden: int, out: int, T: int, stream: int,
                            trace: afd_ffn_trace):
     _check(load_library().afd_ffn_forward_traced(h, hidden, out, T, stream,
                                                  ctypes.byref(trace)))
+
+
+def afd_ffn_forward_static(cfg: afd_ffn_config, w: afd_ffn_weights, hidden: int, out: int,
+                           T: int, stream: int):
+    _check(load_library().afd_ffn_forward_static(ctypes.byref(cfg), ctypes.byref(w), hidden,
+                                                 out, T, stream))
 
 
 def afd_ffn_destroy(h):

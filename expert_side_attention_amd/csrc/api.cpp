@@ -150,6 +150,67 @@ int validate_weights(const afd_ffn_config *c, const afd_ffn_weights *w) {
   return AFD_OK;
 }
 
+// Fill the handle fields that follow from the configuration.
+void init_handle(afd_ffn_handle *h, const afd_ffn_config *cfg, const afd_ffn_weights *w,
+                 int device) {
+  h->cfg = *cfg;
+  h->w = *w;
+  h->device = device;
+  h->elem = cfg->mode == AFD_MODE_F32 ? 0 : (cfg->mode == AFD_MODE_BF16 ? 1 : 2);
+  const int S = cfg->num_shared;
+  h->zpitch = (S > 0 && cfg->shared_inter > cfg->inter) ? cfg->shared_inter : cfg->inter;
+}
+
+// Workspace of forwards of up to T tokens: sets the capacity of the tile
+// lists, points every part at its place above `base` (when not null) and
+// returns the total bytes.  Parts start on 256-byte boundaries.  Allocates
+// nothing.
+size_t layout_workspace(afd_ffn_handle *h, int64_t T, char *base) {
+  const afd_ffn_config &c = h->cfg;
+  const int64_t k = c.top_k, E = c.num_experts, S = c.num_shared, hd = c.hidden;
+  h->tiles_cap = static_cast<int>(tiles_upper_bound(T, c.top_k, c.num_experts, c.num_shared, 16));
+  h->big_cap = static_cast<int>(big_tiles_upper_bound(T, c.top_k, c.num_shared, 256));
+  const int64_t R = T * k + S * T;  // dispatched + shared rows
+  const int zes = h->elem == 0 ? 4 : (h->elem == 1 ? 2 : 1);
+  const int yes = h->elem == 0 ? 4 : 2;
+  struct Part {
+    void **dst;
+    size_t bytes;
+  };
+  Part parts[20];
+  int n = 0;
+  auto add = [&](void *dst, size_t bytes) { parts[n++] = Part{static_cast<void **>(dst), bytes}; };
+  add(&h->ids, sizeof(int32_t) * T * k);
+  add(&h->topk_w, sizeof(float) * T * k);
+  add(&h->slot_row, sizeof(int32_t) * T * k);
+  add(&h->perm, sizeof(int32_t) * T * k);
+  add(&h->counts, sizeof(int32_t) * E);
+  add(&h->offsets, sizeof(int32_t) * (E + 1));
+  add(&h->num_tiles, sizeof(int32_t));
+  add(&h->num_big, sizeof(int32_t));
+  add(&h->counters, 2 * sizeof(int32_t));
+  add(&h->dispatch_scratch, sizeof(int32_t) * 2 * afd::dispatch_blocks(static_cast<int>(T)) * E);
+  add(&h->logits, sizeof(float) * static_cast<size_t>(afd::router_logit_floats(
+                                      static_cast<int>(T), c.hidden, static_cast<int>(E))));
+  add(&h->tiles, sizeof(afd::Tile) * h->tiles_cap);
+  add(&h->tiles_big, sizeof(afd::Tile) * h->big_cap);
+  add(&h->z, static_cast<size_t>(R) * h->zpitch * zes);
+  add(&h->y, static_cast<size_t>(R) * hd * yes);
+  if (h->elem == 2) {
+    add(&h->xq, static_cast<size_t>(T) * hd);
+    add(&h->xs, sizeof(float) * T * (hd / 128));
+    add(&h->zs, sizeof(float) * R * (h->zpitch / 128));
+    add(&h->z32, sizeof(float) * R * h->zpitch);
+  }
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    off = align_up(off, 256);
+    if (base) *parts[i].dst = base + off;
+    off += align_up(parts[i].bytes, 256);
+  }
+  return off;
+}
+
 // Record a profiling event pair around one stage's launches.  Returns the
 // pair's index in the pool (-1: stage not profiled); pairs may nest, so the
 // index, not a pointer into the growing pool, identifies the pair.
@@ -190,54 +251,10 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
   if (rc) return rc;
 
   afd_ffn_handle *h = new afd_ffn_handle();
-  h->cfg = *cfg;
-  h->w = *w;
-  hipGetDevice(&h->device);
-  h->elem = cfg->mode == AFD_MODE_F32 ? 0 : (cfg->mode == AFD_MODE_BF16 ? 1 : 2);
-  const int S = cfg->num_shared;
-  h->zpitch = (S > 0 && cfg->shared_inter > cfg->inter) ? cfg->shared_inter : cfg->inter;
-  const int64_t T = cfg->max_tokens, k = cfg->top_k, E = cfg->num_experts;
-  const int64_t hd = cfg->hidden;
-  h->tiles_cap = static_cast<int>(tiles_upper_bound(T, cfg->top_k, cfg->num_experts, S, 16));
-  h->big_cap = static_cast<int>(big_tiles_upper_bound(T, cfg->top_k, S, 256));
-
-  const int64_t R = T * k + S * T;  // dispatched + shared rows
-  const int zes = h->elem == 0 ? 4 : (h->elem == 1 ? 2 : 1);
-  const int yes = h->elem == 0 ? 4 : 2;
-  struct Part {
-    void **dst;
-    size_t bytes;
-  };
-  std::vector<Part> parts = {
-      {reinterpret_cast<void **>(&h->ids), sizeof(int32_t) * T * k},
-      {reinterpret_cast<void **>(&h->topk_w), sizeof(float) * T * k},
-      {reinterpret_cast<void **>(&h->slot_row), sizeof(int32_t) * T * k},
-      {reinterpret_cast<void **>(&h->perm), sizeof(int32_t) * T * k},
-      {reinterpret_cast<void **>(&h->counts), sizeof(int32_t) * E},
-      {reinterpret_cast<void **>(&h->offsets), sizeof(int32_t) * (E + 1)},
-      {reinterpret_cast<void **>(&h->num_tiles), sizeof(int32_t)},
-      {reinterpret_cast<void **>(&h->num_big), sizeof(int32_t)},
-      {reinterpret_cast<void **>(&h->counters), 2 * sizeof(int32_t)},
-      {reinterpret_cast<void **>(&h->dispatch_scratch),
-       sizeof(int32_t) * 2 * afd::dispatch_blocks(static_cast<int>(T)) * E},
-      {reinterpret_cast<void **>(&h->logits),
-       sizeof(float) * static_cast<size_t>(afd::router_logit_floats(
-                           static_cast<int>(T), cfg->hidden, static_cast<int>(E)))},
-      {reinterpret_cast<void **>(&h->tiles), sizeof(afd::Tile) * h->tiles_cap},
-      {reinterpret_cast<void **>(&h->tiles_big), sizeof(afd::Tile) * h->big_cap},
-      {reinterpret_cast<void **>(&h->z), static_cast<size_t>(R) * h->zpitch * zes},
-      {reinterpret_cast<void **>(&h->y), static_cast<size_t>(R) * hd * yes},
-  };
-  if (h->elem == 2) {
-    parts.push_back({reinterpret_cast<void **>(&h->xq), static_cast<size_t>(T) * hd});
-    parts.push_back({reinterpret_cast<void **>(&h->xs), sizeof(float) * T * (hd / 128)});
-    parts.push_back(
-        {reinterpret_cast<void **>(&h->zs), sizeof(float) * R * (h->zpitch / 128)});
-    parts.push_back(
-        {reinterpret_cast<void **>(&h->z32), sizeof(float) * R * h->zpitch});
-  }
-  size_t total = 0;
-  for (auto &p : parts) total = align_up(total, 256) + align_up(p.bytes, 256);
+  int dev = 0;
+  hipGetDevice(&dev);
+  init_handle(h, cfg, w, dev);
+  const size_t total = layout_workspace(h, cfg->max_tokens, nullptr);
   hipError_t e = hipMalloc(&h->ws, total);
   if (e != hipSuccess) {
     delete h;
@@ -245,12 +262,7 @@ int afd_ffn_create(const afd_ffn_config *cfg, const afd_ffn_weights *w,
     return fail(AFD_ERR_OUT_OF_MEMORY, "workspace of %zu bytes: %s", total, hipGetErrorString(e));
   }
   h->ws_bytes = total;
-  size_t off = 0;
-  for (auto &p : parts) {
-    off = align_up(off, 256);
-    *p.dst = static_cast<char *>(h->ws) + off;
-    off += align_up(p.bytes, 256);
-  }
+  layout_workspace(h, cfg->max_tokens, static_cast<char *>(h->ws));
   *out = h;
   return AFD_OK;
 }
@@ -488,6 +500,35 @@ int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out, int
     if (e != hipSuccess) return hip_fail(e, "trace copy");
   }
   return AFD_OK;
+}
+
+int afd_ffn_forward_static(const afd_ffn_config *cfg, const afd_ffn_weights *w,
+                           const void *hidden, void *out, int64_t T, afd_stream_t stream) {
+  static_assert(AFD_FFN_STATIC_SCRATCH_BYTES == afd::kStaticScratchBytes, "scratch size");
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  rc = validate_weights(cfg, w);
+  if (rc) return rc;
+  if (T < 0) return fail(AFD_ERR_INVALID_ARG, "T = %lld < 0", static_cast<long long>(T));
+  if (T > cfg->max_tokens)
+    return fail(AFD_ERR_CAPACITY, "T = %lld exceeds max_tokens = %d", static_cast<long long>(T),
+                cfg->max_tokens);
+  if (T == 0) return AFD_OK;
+  // the handle lives on this stack frame; its workspace is the scratch array
+  afd_ffn_handle h{};
+  init_handle(&h, cfg, w, -1);
+  const size_t need = layout_workspace(&h, T, nullptr);
+  if (need > afd::kStaticScratchBytes)
+    return fail(AFD_ERR_CAPACITY,
+                "T = %lld needs %zu bytes of scratch, the library holds %zu per device",
+                static_cast<long long>(T), need, afd::kStaticScratchBytes);
+  hipError_t e = hipGetDevice(&h.device);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  void *base = nullptr;
+  e = afd::static_scratch(&base);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  layout_workspace(&h, T, static_cast<char *>(base));
+  return forward_impl(&h, hidden, out, T, static_cast<hipStream_t>(stream), nullptr);
 }
 
 int afd_quant_fp8_1x128(const void *x, int64_t rows, int64_t cols, uint8_t *q, float *s,

@@ -17,6 +17,11 @@ struct Tile {
 };
 
 constexpr int kMaxExperts = 512;
+// Bytes of the per-device scratch array of the allocation-free forward.
+constexpr size_t kStaticScratchBytes = size_t{128} << 20;
+// Device address of this device's scratch array (looked up on the first
+// call per device; allocates nothing).
+hipError_t static_scratch(void **ptr);
 constexpr int kMaxLogitSplits = 16;
 constexpr int kMaxShared = 8;
 

@@ -111,6 +111,7 @@ class FfnLayer:
             num_experts=E, top_k=top_k, inter=I, num_shared=S, shared_inter=Is,
             max_tokens=max_tokens, has_router_bias=int(router_b is not None))
         w = F.afd_ffn_weights(*[_ptr(t) for t in self._keep])
+        self._cfg, self._w = cfg, w
         with torch.cuda.device(dev):
             self._h = F.afd_ffn_create(cfg, w)
 
@@ -159,6 +160,19 @@ class FfnLayer:
         ct = F.afd_ffn_trace(**{n: tr[n].data_ptr() for n in tr})
         F.afd_ffn_forward_traced(self._h, hidden.data_ptr(), out.data_ptr(), T, s, ct)
         return out, tr
+
+    def forward_static(self, hidden: torch.Tensor, out: torch.Tensor = None, stream=None):
+        """The same layer through afd_ffn_forward_static: no handle, the
+        library's fixed per-device scratch as workspace, nothing allocated by
+        the library (out is allocated here when not given)."""
+        T = hidden.shape[0]
+        _need(hidden, "hidden", self.act_dtype, (T, self.hidden), self.device)
+        if out is None:
+            out = torch.empty_like(hidden)
+        _need(out, "out", self.act_dtype, (T, self.hidden), self.device)
+        F.afd_ffn_forward_static(self._cfg, self._w, hidden.data_ptr(), out.data_ptr(), T,
+                                 _stream(stream))
+        return out
 
     def profile_enable(self, stages=()):
         mask = 0

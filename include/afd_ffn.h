@@ -188,6 +188,26 @@ int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out,
                            int64_t T, afd_stream_t stream,
                            const afd_ffn_trace *trace);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward as afd_ffn_forward, same kernels and same results for the same T,
+ * without a handle.  Its workspace is a fixed scratch array of
+ * AFD_FFN_STATIC_SCRATCH_BYTES that the library holds on each device it
+ * runs on, from the first call on that device until the process ends; the
+ * call allocates nothing (the first call on a device only looks up the
+ * array's address).  cfg and w as for create(), read during the call only;
+ * hidden/out as for forward(); 0 <= T <= cfg->max_tokens.  Errors: those of
+ * create() and forward(), and AFD_ERR_CAPACITY when the workspace of T
+ * tokens exceeds the scratch (e.g. 256 tokens of a 4096-wide, 64-expert,
+ * top-8 bf16 layer need 27 MB; 512 tokens of a 7168-wide, 256-expert one
+ * 86 MB).  Every call on one device shares that device's array, which keeps
+ * the last call's contents: calls that overlap in time on one device (two
+ * streams, two threads) race and give wrong results.  Serialise them.      */
+#define AFD_FFN_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+int afd_ffn_forward_static(const afd_ffn_config *cfg, const afd_ffn_weights *w,
+                           const void *hidden, void *out, int64_t T,
+                           afd_stream_t stream);
+
 /* Free the workspace and the handle (waits for the device to finish work
  * that uses it).  The counterpart of create(): the FFN service's state for
  * one layer (vLLM AFD plugin page, "系統架構 / 2. FFN Service").  The
