@@ -255,6 +255,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time the forward captured in a HIP graph and replayed")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="run forwards of at most 16 tokens of a tiny layer as one "
+                         "cooperative launch (the layer's single_launch option)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (profiler calibration)")
     ap.add_argument("--pipeline", action="store_true",
@@ -290,7 +293,7 @@ def main():
     log(f"[bench] building {shape.name} on {dev}")
     nmb = shape.micro_batches
     mbT = shape.T // nmb
-    layer = build_layer(syn, dev, max_tokens=mbT)
+    layer = build_layer(syn, dev, max_tokens=mbT, single_launch=args.single_launch)
     layers = [layer] + [layer.sibling() for _ in range(nmb - 1)]
     x = hidden_tensor(syn, dev)
     xs = [x[i * mbT:(i + 1) * mbT] for i in range(nmb)]
@@ -313,21 +316,25 @@ def main():
     # timed region: K steps; HIP events around the gate/up GEMM launches,
     # recorded on the stream each forward runs on
     for li in layers:
-        li.profile_enable(["gate_up"])
+        li.profile_enable(["gate_up", "single"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gu_ms = gu_n = 0
+    gu_ms = gu_n = one_ms = one_n = 0
     for li in layers:
         prof = li.profile_read()
         li.profile_enable([])
         gu_ms += prof["gate_up"][0]
         gu_n += prof["gate_up"][1]
+        one_ms += prof["single"][0]
+        one_n += prof["single"][1]
     ms_step = (t1 - t0) * 1e3 / args.steps
     gu_avg = gu_ms / max(gu_n, 1)
+    # tiny layers run the whole forward as one launch
+    one_avg = one_ms / one_n if one_n else None
 
     # two micro-batches: the dominant (compute-bound gate/up) launch timed in
     # a serial pass, so that no kernel of the other stream shares its
@@ -351,7 +358,7 @@ def main():
 
     # untimed breakdown of all stages, one micro-batch at a time
     all_stages = ["router", "dispatch", "quant", "gate_up", "down", "combine", "gate_up_big",
-                  "down_big"]
+                  "down_big", "single"]
     stage_tot = {}
     for li in layers:
         li.profile_enable(all_stages)
@@ -406,6 +413,9 @@ def main():
     ridge = MFMA_PEAK_TFLOPS[shape.mode] * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "mfma" if ai > ridge else "hbm"
     gu_launch_bytes = model["gate_up_bytes"] / nmb
+    if one_avg is not None:
+        # the single launch is the whole forward: its bytes are the forward's
+        gu_launch_bytes, gu_avg = model["forward_bytes"], one_avg
     achieved = gu_launch_bytes / (gu_avg * 1e-3) / 1e9
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{shape.name}.json")
@@ -416,12 +426,14 @@ def main():
             traffic = t.get("hbm_bytes_per_launch")
     res_hash = kernel_source_hash()
     if bound == "hbm":
-        roofline = {"bound": "hbm", "kernel": "gate_up grouped GEMM + SwiGLU (weight streaming)",
+        roofline = {"bound": "hbm",
+                    "kernel": ("single-launch forward (fused_small_kernel)" if one_avg is not None
+                               else "gate_up grouped GEMM + SwiGLU (weight streaming)"),
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "avg_launch_ms": round(gu_avg, 5),
                     "algorithmic_bytes_per_launch": int(gu_launch_bytes),
-                    "timed": "HIP events around each gate/up launch in the timed region"}
+                    "timed": "HIP events around each such launch in the timed region"}
     else:
         # compute-bound gate/up launch: unpadded flops of its rows, averaged
         # over the micro-batches' launches (one per micro-batch per step)
@@ -456,7 +468,8 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden states, N(0,0.02) weights; no trained weights)",
         "config": {"workload": shape.name, "T": shape.T, "h": shape.h, "E": shape.E,
                    "k": shape.k, "I": shape.I, "S": shape.S, "Is": shape.Is,
-                   "mode": shape.mode, "seed": args.seed},
+                   "mode": shape.mode, "seed": args.seed,
+                   "single_launch": bool(args.single_launch)},
         "roofline": roofline,
         "forward": {"hbm_gbs": round(fwd_gbs, 1), "hbm_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
                     "bytes": int(model["forward_bytes"]),

@@ -21,7 +21,7 @@ AFD_ERR_CAPACITY, AFD_ERR_OUT_OF_MEMORY, AFD_ERR_HIP = 3, 4, 5
 AFD_MODE_F32, AFD_MODE_BF16, AFD_MODE_W8A8_E4M3 = 0, 1, 2
 AFD_FFN_STATIC_SCRATCH_BYTES = 128 << 20
 STAGES = ("router", "dispatch", "quant", "gate_up", "down", "combine", "gate_up_big",
-          "down_big")
+          "down_big", "single")
 STAGE_INDEX = {n: i for i, n in enumerate(STAGES)}
 
 _STATUS_NAMES = {0: "AFD_OK", 1: "AFD_ERR_INVALID_ARG", 2: "AFD_ERR_UNSUPPORTED",
@@ -39,7 +39,8 @@ class afd_ffn_config(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("num_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
-                ("max_tokens", ctypes.c_int32), ("has_router_bias", ctypes.c_int32)]
+                ("max_tokens", ctypes.c_int32), ("has_router_bias", ctypes.c_int32),
+                ("single_launch", ctypes.c_int32)]
 
 
 class afd_ffn_weights(ctypes.Structure):

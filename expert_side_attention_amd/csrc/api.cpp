@@ -68,6 +68,9 @@ struct afd_ffn_handle {
   float *zs;
   float *z32;  // W8A8 with the streaming kernels: fp32 z before quantisation
   uint8_t *y;
+  // single-launch path of tiny layers (asked for; k <= 16, expert weights
+  // <= 64 MiB)
+  bool fused_ok;
   // profiling
   uint32_t prof_mask;
   std::vector<StageEvents> ev_pool;
@@ -121,6 +124,8 @@ int validate_config(const afd_ffn_config *c) {
     return fail(AFD_ERR_UNSUPPORTED, "an expert matrix must be smaller than 4 GiB in fp32");
   if (c->has_router_bias != 0 && c->has_router_bias != 1)
     return fail(AFD_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
+  if (c->single_launch != 0 && c->single_launch != 1)
+    return fail(AFD_ERR_INVALID_ARG, "single_launch must be 0 or 1");
   return AFD_OK;
 }
 
@@ -159,6 +164,14 @@ void init_handle(afd_ffn_handle *h, const afd_ffn_config *cfg, const afd_ffn_wei
   h->elem = cfg->mode == AFD_MODE_F32 ? 0 : (cfg->mode == AFD_MODE_BF16 ? 1 : 2);
   const int S = cfg->num_shared;
   h->zpitch = (S > 0 && cfg->shared_inter > cfg->inter) ? cfg->shared_inter : cfg->inter;
+  // tiny fp32 / bf16 layers (expert weights of a few MB) run in one launch
+  // for batches of at most kFusedMaxT tokens
+  const int64_t es = h->elem == 0 ? 4 : 2;
+  const int64_t wbytes = (static_cast<int64_t>(cfg->num_experts) * 3 * cfg->inter +
+                          static_cast<int64_t>(S) * 3 * cfg->shared_inter) *
+                         cfg->hidden * es;
+  h->fused_ok = cfg->single_launch == 1 && h->elem != 2 && cfg->top_k <= afd::kFusedMaxK &&
+                wbytes <= afd::kFusedMaxWeightBytes;
 }
 
 // Workspace of forwards of up to T tokens: sets the capacity of the tile
@@ -341,6 +354,50 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   const int Tk = Ti * k;
   hipError_t e;
   int ev;
+
+  // tiny layers, small batches: the whole layer in one cooperative launch
+  // (outside graph capture, where the multi-kernel sequence is recorded)
+  if (h->fused_ok && Ti <= afd::kFusedMaxT) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return hip_fail(e, "capture status");
+    if (cs == hipStreamCaptureStatusNone && afd::fused_supported(h->device)) {
+      afd::FusedArgs fa{};
+      fa.x = static_cast<const uint8_t *>(hidden);
+      fa.wr = static_cast<const uint8_t *>(h->w.router_w);
+      fa.bias = c.has_router_bias ? h->w.router_b : nullptr;
+      fa.gate = static_cast<const uint8_t *>(h->w.gate_w);
+      fa.up = static_cast<const uint8_t *>(h->w.up_w);
+      fa.down = static_cast<const uint8_t *>(h->w.down_w);
+      fa.sgate = static_cast<const uint8_t *>(h->w.sh_gate_w);
+      fa.sup = static_cast<const uint8_t *>(h->w.sh_up_w);
+      fa.sdown = static_cast<const uint8_t *>(h->w.sh_down_w);
+      fa.T = Ti;
+      fa.h = hd;
+      fa.E = E;
+      fa.k = k;
+      fa.I = c.inter;
+      fa.S = S;
+      fa.Is = S > 0 ? c.shared_inter : c.inter;
+      fa.zpitch = h->zpitch;
+      fa.logits = logits_out ? logits_out : h->logits;
+      fa.ids = h->ids;
+      fa.w = h->topk_w;
+      fa.counts = h->counts;
+      fa.offsets = h->offsets;
+      fa.perm = h->perm;
+      fa.slot_row = h->slot_row;
+      fa.num_tiles = h->num_tiles;
+      fa.num_big = h->num_big;
+      fa.z = h->z;
+      fa.out = out;
+      ev = prof_begin(h, AFD_STAGE_SINGLE, s);
+      e = afd::launch_fused_small(h->elem == 0, fa, s);
+      prof_end(h, ev, s);
+      if (e != hipSuccess) return hip_fail(e, "single-launch forward");
+      return AFD_OK;
+    }
+  }
 
   ev = prof_begin(h, AFD_STAGE_ROUTER, s);
   e = afd::launch_router(h->elem == 0, hidden, h->w.router_w,

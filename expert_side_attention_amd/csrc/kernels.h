@@ -123,6 +123,30 @@ int logits_splits(int T, int h, int E);
 hipError_t launch_logits_gemm(const uint16_t *x, const uint16_t *wr, int T, int h, int E,
                               float *partials, int splits, hipStream_t s);
 
+// Single-launch forward of tiny fp32 / bf16 layers (cooperative grid with
+// one grid-wide barrier).  Limits: T <= kFusedMaxT, k <= kFusedMaxK; I and
+// I_s multiples of 128; z holds T k + S T rows of zpitch elements of the
+// layer's type.  ids ... num_big receive the routing and dispatch (as the
+// multi-kernel forward's workspace holds them).
+constexpr int kFusedMaxT = 16;
+constexpr int kFusedMaxK = 16;
+constexpr int kFusedMaxGrid = 256;
+constexpr int64_t kFusedMaxWeightBytes = int64_t{64} << 20;
+struct FusedArgs {
+  const uint8_t *x, *wr;
+  const float *bias;
+  const uint8_t *gate, *up, *down, *sgate, *sup, *sdown;
+  int T, h, E, k, I, S, Is, zpitch;
+  float *logits;
+  int32_t *ids;
+  float *w;
+  int32_t *counts, *offsets, *perm, *slot_row, *num_tiles, *num_big;
+  uint8_t *z;
+  void *out;
+};
+bool fused_supported(int device);
+hipError_t launch_fused_small(bool f32, const FusedArgs &a, hipStream_t s);
+
 // out[t] = sum_j w[t,j] Y[slot_row[t,j]] + sum_s Y[Tk + s*T + t].
 hipError_t launch_combine(bool f32, const uint8_t *Y, const int32_t *slot_row,
                           const float *w, int T, int k, int S, int h,

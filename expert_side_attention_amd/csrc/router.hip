@@ -15,6 +15,7 @@
 // workgroup per 16 tokens, top-k in the same kernel.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace afd {
 namespace {
@@ -24,32 +25,6 @@ namespace {
 // 74 us with the top-k's loads hoisted; at 2048 the register-operand kernel
 // below is faster, 55 against 76 us)
 constexpr int kTiledRouterT = 4096;
-
-// Sortable key: larger logit first, then smaller index.  Key 0 = removed.
-__device__ __forceinline__ unsigned long long topk_key(float v, int e) {
-  v += 0.0f;  // -0 -> +0 so equal logits compare equal
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<unsigned long long>(u) << 32) |
-         static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(e));
-}
-
-// The logit a key was made from (-0 comes back as +0).
-__device__ __forceinline__ float topk_key_value(unsigned long long key) {
-  const uint32_t u = static_cast<uint32_t>(key >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), o, 64);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), o, 64);
-    unsigned long long y = (static_cast<unsigned long long>(hi) << 32) | lo;
-    x = y > x ? y : x;
-  }
-  return x;
-}
 
 // Top-k over the logits of TM tokens (row pitch E, in LDS or global memory),
 // one wave per token at a time.  NC = candidates per lane (E <= 64 * NC).

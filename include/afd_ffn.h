@@ -90,6 +90,10 @@ typedef struct {
   int32_t shared_inter;   /* I_s                                             */
   int32_t max_tokens;     /* largest T passed to forward(); sizes workspace  */
   int32_t has_router_bias;/* 1: router_b is added to the logits              */
+  int32_t single_launch;  /* 1: run forwards of at most 16 tokens of a tiny
+                             fp32 / bf16 layer (top_k <= 16, expert weights
+                             <= 64 MiB) as one cooperative launch (outside
+                             graph capture); 0: the kernel sequence          */
 } afd_ffn_config;
 
 /* Weight pointers (device, borrowed).  The experts are SwiGLU matrix
@@ -253,8 +257,9 @@ int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols,
  * caller), then resets.  Errors: NULL handle or arrays, unknown bits ->
  * AFD_ERR_INVALID_ARG; a failed event -> AFD_ERR_HIP.  The compute-bound
  * launches of the gate/up and down stages (256-row tiles) are also timed
- * on their own under AFD_STAGE_GATE_UP_BIG and AFD_STAGE_DOWN_BIG.  Stage
- * bits:                                                                    */
+ * on their own under AFD_STAGE_GATE_UP_BIG and AFD_STAGE_DOWN_BIG; a forward
+ * that runs as one launch (tiny layers, at most 16 tokens) is timed under
+ * AFD_STAGE_SINGLE only.  Stage bits:                                                                    */
 #define AFD_STAGE_ROUTER   0
 #define AFD_STAGE_DISPATCH 1
 #define AFD_STAGE_QUANT    2
@@ -263,7 +268,8 @@ int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols,
 #define AFD_STAGE_COMBINE  5
 #define AFD_STAGE_GATE_UP_BIG 6
 #define AFD_STAGE_DOWN_BIG 7
-#define AFD_STAGE_COUNT    8
+#define AFD_STAGE_SINGLE   8  /* the single-launch forward of tiny layers */
+#define AFD_STAGE_COUNT    9
 int afd_ffn_profile_enable(afd_ffn_handle *h, uint32_t stage_mask);
 int afd_ffn_profile_read(afd_ffn_handle *h, double *ms /*[AFD_STAGE_COUNT]*/,
                          int64_t *launches /*[AFD_STAGE_COUNT]*/);

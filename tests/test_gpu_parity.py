@@ -25,10 +25,10 @@ def _np(t):
     return t.numpy()
 
 
-def run_gpu(syn, x_store=None, max_tokens=None, layer=None):
+def run_gpu(syn, x_store=None, max_tokens=None, layer=None, single_launch=False):
     from expert_side_attention_amd.workload import build_layer, to_device
     s = syn.shape
-    layer = layer or build_layer(syn, DEV, max_tokens=max_tokens)
+    layer = layer or build_layer(syn, DEV, max_tokens=max_tokens, single_launch=single_launch)
     x = syn.hidden() if x_store is None else x_store
     xt = to_device(x, DEV, s.mode != "f32")
     out, tr = layer.forward(xt, trace=True)
@@ -36,11 +36,11 @@ def run_gpu(syn, x_store=None, max_tokens=None, layer=None):
     return layer, _np(out), {k: v.cpu().numpy() for k, v in tr.items()}
 
 
-def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False):
+def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False, single_launch=False):
     s = syn.shape
     x = syn.hidden() if x_store is None else x_store
-    print(f"[parity] {s}", flush=True)
-    _, out, tr = run_gpu(syn, x)
+    print(f"[parity] {s} single_launch={single_launch}", flush=True)
+    _, out, tr = run_gpu(syn, x, single_launch=single_launch)
     orc = O.OracleFFN(syn, threads=threads)
     ref = orc.forward(x)
     x64 = decode_store(x, s.mode)
@@ -103,7 +103,17 @@ SMALL = [
     LayerShape("bf16_prefill_h384", T=520, h=384, E=4, k=2, I=256, S=1, Is=128, mode="bf16"),
     LayerShape("bf16_prefill_skew", T=1500, h=256, E=16, k=2, I=256, S=1, Is=256,
                mode="bf16", router="zipf"),
+    # tiny layers, at most 16 tokens, also run as one launch (FUSED below)
+    LayerShape("fused_bf16_shared", T=13, h=512, E=32, k=6, I=256, S=2, Is=128, mode="bf16"),
+    LayerShape("fused_bf16_e512_k16", T=7, h=128, E=512, k=16, I=128, S=1, Is=256,
+               mode="bf16", router="zipf"),
+    LayerShape("fused_f32_t1", T=1, h=128, E=4, k=4, I=128, S=1, Is=128, mode="f32"),
+    LayerShape("fused_f32_h384", T=16, h=384, E=16, k=3, I=384, S=1, Is=128, mode="f32"),
 ]
+
+# shapes also checked with single_launch = 1 (tile lists then stay empty)
+FUSED = {"tiny_fp32", "fused_bf16_shared", "fused_bf16_e512_k16", "fused_f32_t1",
+         "fused_f32_h384"}
 
 
 # long batches at small width: 64 dispatch blocks, large tile lists and grids,
@@ -124,7 +134,47 @@ def test_long_batch_parity(shape):
 
 @pytest.mark.parametrize("shape", SMALL, ids=[s.name for s in SMALL])
 def test_small_layer_parity(shape):
-    check_layer(SyntheticLayer(shape, seed=3))
+    _, tr, _ = check_layer(SyntheticLayer(shape, seed=3))
+    # the kernel sequence has at least one weight-streaming or tiled row tile
+    assert tr["num_tiles"][0] > 0 or tr["num_tiles"][1] > 0
+
+
+@pytest.mark.parametrize("shape", [s for s in SMALL if s.name in FUSED],
+                         ids=lambda s: s.name)
+def test_single_launch_parity(shape):
+    """The same tiny layers run as one cooperative launch: the same parity
+    rules, and no GEMM tile lists (the single-launch path builds none)."""
+    _, tr, _ = check_layer(SyntheticLayer(shape, seed=3), single_launch=True,
+                           expect_exact_routing=shape.name == "tiny_fp32")
+    assert tr["num_tiles"].tolist() == [0, 0]
+
+
+@pytest.mark.parametrize("shape", [
+    LayerShape("rep_fused_bf16", T=16, h=256, E=16, k=4, I=256, S=1, Is=256, mode="bf16"),
+    LayerShape("rep_fused_f32", T=9, h=256, E=8, k=2, I=512, mode="f32"),
+], ids=lambda s: s.name)
+def test_single_launch_path_repeats_and_splits(shape):
+    """The single-launch forward: bitwise repeatable, and a token's result
+    does not depend on the other tokens of the batch (any batch of at most
+    16 tokens takes the same path)."""
+    syn = SyntheticLayer(shape, seed=23)
+    from expert_side_attention_amd.workload import build_layer, to_device
+    layer = build_layer(syn, DEV, single_launch=True)
+    x = to_device(syn.hidden(), DEV, shape.mode != "f32")
+    iv = torch.int32 if shape.mode == "f32" else torch.int16
+    ref, tr = layer.forward(x, trace=True)
+    ref = ref.clone()
+    assert tr["num_tiles"].tolist() == [0, 0]
+    out = torch.empty_like(ref)
+    for i in range(12):
+        layer.forward(x, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(iv), ref.view(iv)), f"forward {i}"
+    a = layer.forward(x[:5].contiguous()).clone()
+    b = layer.forward(x[5:].contiguous()).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a, b]).view(iv), ref.view(iv))
+    layer.close()
 
 
 def test_tiny_fp32_is_fp32_accurate():

@@ -19,12 +19,14 @@ DEV = "cuda:0"
     (LayerShape("na_bf16_prefill", T=600, h=512, E=16, k=4, I=256, S=1, Is=256, mode="bf16"), 33),
     (LayerShape("na_w8a8", T=256, h=512, E=16, k=4, I=256, S=1, Is=384, mode="w8a8"), 50),
     (LayerShape("na_f32", T=64, h=256, E=8, k=2, I=256, S=1, Is=128, mode="f32"), 5),
+    # one cooperative launch per forward (single_launch = 1)
+    (LayerShape("na_single_f32", T=16, h=256, E=8, k=2, I=512, mode="f32"), 5),
 ], ids=lambda v: v.name if hasattr(v, "name") else str(v))
 def test_static_forward_matches_handle_forward(shape, T2):
     from expert_side_attention_amd.workload import build_layer, hidden_tensor
     print(f"[no-alloc] {shape.name} T={shape.T} then T={T2}", flush=True)
     syn = SyntheticLayer(shape, seed=17)
-    layer = build_layer(syn, DEV)
+    layer = build_layer(syn, DEV, single_launch=shape.name.startswith("na_single"))
     x = hidden_tensor(syn, DEV)
     iv = torch.int32 if shape.mode == "f32" else torch.int16
     for T in (shape.T, T2):
