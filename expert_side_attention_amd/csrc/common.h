@@ -137,4 +137,27 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) {
   *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// acc (16 rows x 16 columns) += A[rows][K] . B[cols][K]^T over nck 128-byte
+// K chunks; lane (r16, q) supplies row / column r16 and bytes [32 q, 32 q +
+// 32) of each chunk; arow / brow point at the lane's row and column.
+template <Elem EL>
+__device__ __forceinline__ f32x4 mma_rows(const uint8_t *arow, const uint8_t *brow, int nck,
+                                          f32x4 acc) {
+  for (int k0 = 0; k0 < nck; k0 += 4) {
+    Frag32 fa[4], fb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kc = (k0 + u < nck ? k0 + u : k0) * 128;
+      fa[u].lo = ld16(arow + kc);
+      fa[u].hi = ld16(arow + kc + 16);
+      fb[u].lo = ld16(brow + kc);
+      fb[u].hi = ld16(brow + kc + 16);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + u < nck) acc = mma32<EL>(fa[u], fb[u], acc);
+  }
+  return acc;
+}
+
 }  // namespace afd

@@ -209,27 +209,59 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
                       planes, static_cast<int64_t>(T) * E, bias, lout);
 }
 
-// fp32 router for small layers: one (token, expert) dot product per thread.
+// fp32 router for small layers: 16 tokens per workgroup, 16 experts per
+// 16x16 fp32 MFMA block; the four waves take quarters of K (loads issued in
+// batches) and add their partial logits into LDS in wave order, so the
+// logits do not depend on timing; then the top-k from LDS.
 template <int TM>
 __global__ __launch_bounds__(256) void router_f32_kernel(
     const float *__restrict__ X, const float *__restrict__ Wr,
     const float *__restrict__ bias, int T, int h, int E, int k,
     int32_t *__restrict__ ids, float *__restrict__ wout, float *__restrict__ lout) {
+  static_assert(TM == 16, "one 16-row MFMA block of tokens");
   __shared__ float sl[TM * kMaxExperts];
   __shared__ float selv[4 * kMaxExperts];
   const int t0 = blockIdx.x * TM;
-  for (int p = threadIdx.x; p < TM * E; p += 256) {
-    const int tt = p / E, e = p % E, t = t0 + tt;
-    float a = 0.0f;
-    if (t < T) {
-      const float *xr = X + static_cast<int64_t>(t) * h;
-      const float *wr = Wr + static_cast<int64_t>(e) * h;
-      for (int i = 0; i < h; ++i) a = fmaf(xr[i], wr[i], a);
-      if (bias) a += bias[e];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int64_t xrow = static_cast<int64_t>(h) * 4;
+  const int nck = static_cast<int>(xrow / 128);  // 128-byte K chunks of a row
+  const int c0 = wave * nck / 4, c1 = (wave + 1) * nck / 4;
+  const int tr = t0 + r16 < T ? t0 + r16 : T - 1;  // rows past T repeat the last token
+  const uint8_t *xa = reinterpret_cast<const uint8_t *>(X) + tr * xrow + q * 32 + c0 * 128;
+  constexpr int NB = kMaxExperts / 16;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int eb = 0; eb < NB; ++eb) {
+    acc[eb] = f32x4{0, 0, 0, 0};
+    if (eb * 16 < E) {
+      const int e = eb * 16 + r16 < E ? eb * 16 + r16 : E - 1;
+      acc[eb] = mma_rows<Elem::F32>(
+          xa, reinterpret_cast<const uint8_t *>(Wr) + e * xrow + q * 32 + c0 * 128, c1 - c0,
+          acc[eb]);
     }
-    sl[tt * E + e] = a;
   }
-  __syncthreads();
+  // lane holds tokens 4 q + i, expert eb * 16 + r16; waves add in order
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int eb = 0; eb < NB; ++eb) {
+        const int e = eb * 16 + r16;
+        if (eb * 16 < E && e < E) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float *d = &sl[(4 * q + i) * E + e];
+            *d = w == 0 ? acc[eb][i] : *d + acc[eb][i];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (bias) {
+    for (int p = threadIdx.x; p < TM * E; p += 256) sl[p] += bias[p % E];
+    __syncthreads();
+  }
   topk_rows<TM, kMaxExperts / 64>(sl, selv, t0, T, E, k, ids, wout, 1, 0, nullptr, lout);
 }
 
