@@ -7,32 +7,33 @@
 // Tile: 256 rows x 256 weight rows per workgroup (gate/up: 128 gate + 128 up
 // rows, i.e. 128 output columns of z; down: 256 output columns), K in
 // 64-element (128-byte) stages, so every load request is a whole cache line.
-// Eight waves (two per SIMD) in a 2 x 4 grid each own 128 rows x 64 weight
-// rows = 4 x 2 tiles of 32x32x16 MFMAs (128 fp32 accumulators per lane); for
-// gate/up a wave's two column blocks are a gate block and the up block of
-// the same columns.
 //
 // Operands move with direct-to-LDS loads (global_load_lds, no staging
 // registers) into two 64 KB stage buffers: the next stage loads while the
-// MFMAs read the current one, its loads issued one at a time between the
-// first K steps' MFMAs.  Ordering uses an explicit vmcnt(0) wait plus a
-// bare s_barrier per stage (a full workgroup fence would drain every
+// MFMAs read the current one.  Ordering uses an explicit vmcnt(0) wait plus
+// a bare s_barrier per stage (a full workgroup fence would drain every
 // outstanding load).  The wait is for zero on purpose: with several stages
 // of direct-to-LDS loads in flight, a wait that leaves the newest loads
-// outstanding did not guarantee that the older ones had landed in LDS (a
-// deeper ring built that way gave run-to-run different results).  LDS rows are 128 bytes with the 16-byte chunk index XOR-ed by
-// (row / 2) % 8, so the 16 rows one MFMA operand read touches per quarter
-// wave hit 16 different 4-bank groups.  (32-element stages in a deeper ring
-// fetched half lines and ran 7-9% slower.)
+// outstanding does not guarantee that the older ones have landed in LDS (a
+// probe of that scheme read stale data a few times per billion reads).  LDS
+// rows are 128 bytes with the 16-byte chunk index XOR-ed by (row / 2) % 8, so
+// the 16 rows one MFMA operand read touches per quarter wave hit 16
+// different 4-bank groups.
 //
 // Tile order: row tiles are dealt round-robin to the 8 XCDs (workgroup ids
 // go to XCDs round-robin) and all column tiles of a row tile run on one XCD,
 // close in time: the XCD's L2 serves the activation rows to all of them.
 //
-// The same kernel also computes router logits of long batches (logits
-// mode): rows of X against the router weight, the K range split over
-// workgroups, fp32 partial sums written straight from the accumulators to
-// one plane per split (the top-k kernel adds the planes).
+// Two kernels share this layout.  The expert GEMMs run on four waves (one
+// per SIMD), each owning 128 rows x 128 weight rows as 8 x 8 tiles of
+// 16x16x32 MFMAs with a hand-fixed instruction order (prefill_gemm4_kernel,
+// below).  The router logits of long batches (logits mode: rows of X
+// against the router weight, the K range split over workgroups, fp32
+// partial sums written straight from the accumulators to one plane per
+// split, which the top-k kernel adds) run on eight waves (two per SIMD) in a
+// 2 x 4 grid, each owning 128 rows x 64 weight rows = 4 x 2 tiles of
+// 32x32x16 MFMAs, the next stage's loads issued one at a time between the
+// first K steps' MFMAs (prefill_gemm_kernel).
 #include "common.h"
 #include <atomic>
 
@@ -258,18 +259,201 @@ __global__ __launch_bounds__(512) void prefill_gemm_kernel(const GemmArgs p) {
   }
 }
 
+// Four-wave kernel (one wave per SIMD) of the expert GEMMs: the tile, stage
+// layout, loads and tile order above, each wave owning 128 rows x 128
+// weight rows as 8 x 8 tiles of 16x16x32 MFMAs (256 accumulators per lane,
+// in the accumulation registers), so a stage reads half the LDS fragments
+// per MFMA of the eight-wave layout.  With one wave per SIMD the wave keeps
+// its matrix core fed by itself, so the instruction order is fixed by hand
+// with scheduling fences; the schedule is described at the main loop.
 template <int MODE>
-hipError_t set_lds_limit() {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_gemm4_kernel(const GemmArgs p) {
+  constexpr bool SWIGLU = MODE == kGateUp;
+  extern __shared__ __align__(16) uint8_t lds[];  // kRing x (A 32 KB + B 32 KB)
+  __shared__ int rowsrc[kBM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;  // 2 x 2 waves: 128 rows x 128 weight rows each
+  const int r16 = lane & 15, q = lane >> 4;
+  constexpr int BNO = SWIGLU ? kBW / 2 : kBW;  // output columns per tile
+
+  const int nmax = p.N > p.Ns ? p.N : p.Ns;
+  const int ntn = (nmax + BNO - 1) / BNO;
+  const int L = blockIdx.x;
+  const int j = L >> 3;
+  const int mt = (L & 7) + 8 * (j / ntn);
+  const int nt = j % ntn;
+  if (mt >= *p.num_tiles) return;
+  const Tile tile = p.tiles[mt];
+  const bool shared = tile.group >= p.E;
+  const int N = shared ? p.Ns : p.N;
+  const int K = shared ? p.Ks : p.K;
+  const int n0 = nt * BNO;
+  if (n0 >= N) return;
+  const int gi = shared ? tile.group - p.E : tile.group;
+  const int rows = tile.rows;
+
+  {
+    int src = -1;
+    if (tid < rows) {
+      const int r = tile.row0 + tid;
+      src = p.perm ? (r < p.Tk ? p.perm[r] : (r - p.Tk) % p.T) : r;
+    }
+    rowsrc[tid] = src;  // 256 threads, 256 rows
+  }
+  __syncthreads();
+
+  const int64_t krow = static_cast<int64_t>(K) * 2;
+  const int nst = static_cast<int>(krow / kStage);
+  const int64_t mat = static_cast<int64_t>(N) * krow;
+  const uint8_t *B0 = (shared ? p.sb0 : p.b0) + gi * mat;
+  const uint8_t *B1 = SWIGLU ? (shared ? p.sb1 : p.b1) + gi * mat : B0;
+
+  // wave w moves rows [64 w, 64 w + 64) of the A stage and of the B stage:
+  // eight 1 KB direct-to-LDS loads each (layout and swizzle as above); the
+  // wave's B rows are 64 consecutive weight rows of one matrix
+  const int src_first = rowsrc[0];
+  const uint8_t *asrc[8];
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) {
+    const int row = wave * 64 + hh * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);
+    const int src = rowsrc[row] >= 0 ? rowsrc[row] : src_first;
+    asrc[hh] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
+  }
+  const uint8_t *bsrc[8];
+  {
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+      const int row = wave * 64 + hh * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ ((row >> 1) & 7);
+      const int n = n0 + (SWIGLU ? (row & (kBW / 2 - 1)) : row);
+      const uint8_t *base = (SWIGLU && wave >= 2) ? B1 : B0;
+      bsrc[hh] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16;
+    }
+  }
+  // load jj (0..15) of stage t: jj < 8 -> A rows block jj, else B rows block jj - 8
+  auto load = [&](int t, int jj) {
+    uint8_t *slot = lds + (t % kRing) * kSlot;
+    if (jj < 8)
+      dma16(asrc[jj] + static_cast<int64_t>(t) * kStage, slot + (wave * 8 + jj) * 1024);
+    else
+      dma16(bsrc[jj - 8] + static_cast<int64_t>(t) * kStage,
+            slot + kBM * kStage + (wave * 8 + jj - 8) * 1024);
+  };
+
+  // this wave's weight rows: gate/up -> 64 gate rows (blocks 0-3) and the up
+  // rows of the same columns (blocks 4-7); down -> 128 rows
+  auto wrow = [&](int n) {
+    return SWIGLU ? (n < 4 ? wc * 64 + n * 16 : kBW / 2 + wc * 64 + (n - 4) * 16) + r16
+                  : wc * 128 + n * 16 + r16;
+  };
+  // fragments: one register set per 32-element K step (set kk for step kk)
+  bf16x8 fa[2][8], fb[2][8];
+  // fragment jj (0..15: A blocks, then B blocks) of K step kk of stage t
+  auto read = [&](int t, int kk, int jj) {
+    const uint8_t *la = lds + (t % kRing) * kSlot;
+    if (jj < 8)
+      fa[kk][jj] = bitcast<bf16x8>(ld16(la + swz64(wr * 128 + jj * 16 + r16, kk * 4 + q)));
+    else
+      fb[kk][jj - 8] =
+          bitcast<bf16x8>(ld16(la + kBM * kStage + swz64(wrow(jj - 8), kk * 4 + q)));
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
+
+  // Schedule of stage s: K step 0 on set 0 while set 1 is read (step 1 of
+  // the same stage, one read per two MFMAs in the first half); then every
+  // wave waits for its loads of stage s + 1 and meets the others at the
+  // barrier, after which nothing reads stage s from LDS any more; K step 1
+  // on set 1 while the sixteen loads of stage s + 2 go into stage s's
+  // buffer, one per four MFMAs, and set 0 is read from stage s + 1.  A load
+  // thus has about one stage to arrive.  Measured alternatives were slower:
+  // the loads packed into the first quarter or half of step 1, or the
+  // barrier 16 MFMAs before the end of step 0 (which also made the register
+  // allocator move accumulators between register files inside the loop).
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) load(0, jj);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) read(0, 0, jj);
+  if (nst > 1) {
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) load(1, jj);
+  }
+
+  for (int s = 0; s < nst; ++s) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int m = i >> 3, n = i & 7;
+      acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[0][m], fb[0][n], acc[m][n], 0, 0, 0);
+      if ((i & 1) == 1 && i < 32) read(s, 1, i >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const bool load2 = s + 2 < nst, read1 = s + 1 < nst;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int m = i >> 3, n = i & 7;
+      acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][m], fb[1][n], acc[m][n], 0, 0, 0);
+      if ((i & 3) == 0 && load2) load(s + 2, i >> 2);
+      if ((i & 1) == 1 && i < 32 && read1) read(s + 1, 0, i >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();  // every wave is done with the ring before the epilogue reuses it
+
+  // ---- epilogue: stage the bf16 tile in LDS, then whole 16-byte stores.
+  // acc[m][n][i]: row wr*128 + 16 m + 4 q + i, weight row block n, column r16.
+  uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
+  constexpr int OPITCH = BNO;
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wr * 128 + m * 16 + 4 * q + i;
+      if (SWIGLU) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          o16[row * OPITCH + wc * 64 + n * 16 + r16] =
+              f32_to_bf16(silu_mul(acc[m][n][i], acc[m][n + 4][i]));
+      } else {
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+          o16[row * OPITCH + wc * 128 + n * 16 + r16] = f32_to_bf16(acc[m][n][i]);
+      }
+    }
+  __syncthreads();
+  constexpr int CPR = OPITCH * 2 / 16;
+  const int vcpr = min(CPR, (N - n0) * 2 / 16);
+  for (int c = tid; c < kBM * CPR; c += 256) {
+    const int row = c / CPR, col = c % CPR;
+    if (row < rows && col < vcpr)
+      st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
+           ld16(lds + row * OPITCH * 2 + col * 16));
+  }
+}
+
+// the dynamic-LDS limit is a per-device attribute of each kernel
+template <typename KernelFn>
+hipError_t set_lds_limit(KernelFn kern, std::atomic<bool> (&attr_set)[64]) {
   constexpr size_t kLds = kRing * kSlot;  // 2 x 64 KB
-  // the dynamic-LDS limit is a per-device attribute of the kernel
-  constexpr int kMaxDevices = 64;
-  static std::atomic<bool> attr_set[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!attr_set[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_gemm_kernel<MODE>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     attr_set[dev].store(true, std::memory_order_release);
@@ -278,15 +462,22 @@ hipError_t set_lds_limit() {
 }
 
 template <int MODE>
+hipError_t set_lds_limit() {
+  static std::atomic<bool> attr_set[64];
+  return set_lds_limit(prefill_gemm_kernel<MODE>, attr_set);
+}
+
+template <int MODE>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = MODE == kGateUp ? kBW / 2 : kBW;
-  hipError_t e = set_lds_limit<MODE>();
+  static std::atomic<bool> attr_set[64];
+  hipError_t e = set_lds_limit(prefill_gemm4_kernel<MODE>, attr_set);
   if (e != hipSuccess) return e;
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int ntn = (nmax + BNO - 1) / BNO;
   const int64_t grid = 8LL * ((a.tiles_ub + 7) / 8) * ntn;
   if (grid <= 0) return hipSuccess;
-  prefill_gemm_kernel<MODE><<<static_cast<unsigned>(grid), 512, kRing * kSlot, s>>>(a);
+  prefill_gemm4_kernel<MODE><<<static_cast<unsigned>(grid), 256, kRing * kSlot, s>>>(a);
   return hipGetLastError();
 }
 
