@@ -456,7 +456,7 @@ def main():
         tf = flops / (avg * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[shape.mode]
         roofline = {"bound": "mfma",
-                    "kernel": "gate_up grouped GEMM + SwiGLU, 256-row tiles (prefill_gemm_kernel<1>)",
+                    "kernel": "gate_up grouped GEMM + SwiGLU, 256-row tiles (prefill_gemm4_kernel<1>)",
                     "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tf / peak, 4), "traffic": traffic,
                     "avg_launch_ms": round(avg, 5),
