@@ -343,6 +343,19 @@ void prefill_gemm4_kernel(const GemmArgs p) {
       dma16(bsrc[jj - 8] + static_cast<int64_t>(t) * kStage,
             slot + kBM * kStage + (wave * 8 + jj - 8) * 1024);
   };
+  // the same from pointers that advance one stage per use, up to the last
+  // stage (past it the last stage is loaded again, into a buffer nothing
+  // reads any more)
+  auto load_next = [&](int slot_idx, int jj, int64_t adv) {
+    uint8_t *slot = lds + slot_idx * kSlot;
+    if (jj < 8) {
+      dma16(asrc[jj], slot + (wave * 8 + jj) * 1024);
+      asrc[jj] += adv;
+    } else {
+      dma16(bsrc[jj - 8], slot + kBM * kStage + (wave * 8 + jj - 8) * 1024);
+      bsrc[jj - 8] += adv;
+    }
+  };
 
   // this wave's weight rows: gate/up -> 64 gate rows (blocks 0-3) and the up
   // rows of the same columns (blocks 4-7); down -> 128 rows
@@ -374,7 +387,10 @@ void prefill_gemm4_kernel(const GemmArgs p) {
   // barrier, after which nothing reads stage s from LDS any more; K step 1
   // on set 1 while the sixteen loads of stage s + 2 go into stage s's
   // buffer, one per four MFMAs, and set 0 is read from stage s + 1.  A load
-  // thus has about one stage to arrive.  Measured alternatives were slower:
+  // thus has about one stage to arrive.  The loop has no branches: the
+  // loads advance their own pointers and, past the last stage, repeat it
+  // (about 32 branches per stage around conditional loads had cost ~8%).
+  // Measured alternatives were slower:
   // the loads packed into the first quarter or half of step 1, or the
   // barrier 16 MFMAs before the end of step 0 (which also made the register
   // allocator move accumulators between register files inside the loop).
@@ -389,6 +405,15 @@ void prefill_gemm4_kernel(const GemmArgs p) {
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) load(1, jj);
   }
+  // the pointers now address stage 2 (or the last stage)
+  {
+    const int64_t first = static_cast<int64_t>(min(2, nst - 1)) * kStage;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      asrc[jj] += first;
+      bsrc[jj] += first;
+    }
+  }
 
   for (int s = 0; s < nst; ++s) {
 #pragma unroll
@@ -401,16 +426,20 @@ void prefill_gemm4_kernel(const GemmArgs p) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const bool load2 = s + 2 < nst, read1 = s + 1 < nst;
+    // past the last stage the loads and reads repeat it (in bounds, unused)
+    const int s1 = min(s + 1, nst - 1);
+    const int64_t adv = s + 3 < nst ? kStage : 0;
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       const int m = i >> 3, n = i & 7;
       acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][m], fb[1][n], acc[m][n], 0, 0, 0);
-      if ((i & 3) == 0 && load2) load(s + 2, i >> 2);
-      if ((i & 1) == 1 && i < 32 && read1) read(s + 1, 0, i >> 1);
+      if ((i & 3) == 0) load_next(s & 1, i >> 2, adv);
+      if ((i & 1) == 1 && i < 32) read(s1, 0, i >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // the repeated loads of the last stage may still be landing in LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // every wave is done with the ring before the epilogue reuses it
 
   // ---- epilogue: stage the bf16 tile in LDS, then whole 16-byte stores.
