@@ -445,7 +445,9 @@ void prefill_gemm4_kernel(const GemmArgs p) {
   // ---- epilogue: stage the bf16 tile in LDS, then whole 16-byte stores.
   // acc[m][n][i]: row wr*128 + 16 m + 4 q + i, weight row block n, column r16.
   uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
-  constexpr int OPITCH = BNO;
+  // staged rows padded by 16 bytes: the four rows a store touches (4 apart)
+  // then fall in different LDS banks
+  constexpr int OPITCH = BNO + 8;
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -463,7 +465,7 @@ void prefill_gemm4_kernel(const GemmArgs p) {
       }
     }
   __syncthreads();
-  constexpr int CPR = OPITCH * 2 / 16;
+  constexpr int CPR = BNO * 2 / 16;  // 16-byte pieces of data per staged row
   const int vcpr = min(CPR, (N - n0) * 2 / 16);
   for (int c = tid; c < kBM * CPR; c += 256) {
     const int row = c / CPR, col = c % CPR;
@@ -475,8 +477,8 @@ void prefill_gemm4_kernel(const GemmArgs p) {
 
 // the dynamic-LDS limit is a per-device attribute of each kernel
 template <typename KernelFn>
-hipError_t set_lds_limit(KernelFn kern, std::atomic<bool> (&attr_set)[64]) {
-  constexpr size_t kLds = kRing * kSlot;  // 2 x 64 KB
+hipError_t set_lds_limit(KernelFn kern, std::atomic<bool> (&attr_set)[64],
+                         size_t kLds = kRing * kSlot) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -496,17 +498,26 @@ hipError_t set_lds_limit() {
   return set_lds_limit(prefill_gemm_kernel<MODE>, attr_set);
 }
 
+// dynamic LDS of the four-wave kernel: the two stage buffers, or the padded
+// output tile of the epilogue if that is larger (down: 256 x 264 bf16)
+template <int MODE>
+constexpr size_t lds4_bytes() {
+  constexpr size_t ring = kRing * kSlot;
+  constexpr size_t out = static_cast<size_t>(kBM) * ((MODE == kGateUp ? kBW / 2 : kBW) + 8) * 2;
+  return ring > out ? ring : out;
+}
+
 template <int MODE>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = MODE == kGateUp ? kBW / 2 : kBW;
   static std::atomic<bool> attr_set[64];
-  hipError_t e = set_lds_limit(prefill_gemm4_kernel<MODE>, attr_set);
+  hipError_t e = set_lds_limit(prefill_gemm4_kernel<MODE>, attr_set, lds4_bytes<MODE>());
   if (e != hipSuccess) return e;
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int ntn = (nmax + BNO - 1) / BNO;
   const int64_t grid = 8LL * ((a.tiles_ub + 7) / 8) * ntn;
   if (grid <= 0) return hipSuccess;
-  prefill_gemm4_kernel<MODE><<<static_cast<unsigned>(grid), 256, kRing * kSlot, s>>>(a);
+  prefill_gemm4_kernel<MODE><<<static_cast<unsigned>(grid), 256, lds4_bytes<MODE>(), s>>>(a);
   return hipGetLastError();
 }
 
