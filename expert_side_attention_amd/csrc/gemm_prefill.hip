@@ -323,13 +323,23 @@ void prefill_gemm4_kernel(const GemmArgs p) {
     const int src = rowsrc[row] >= 0 ? rowsrc[row] : src_first;
     asrc[hh] = p.A + static_cast<int64_t>(src) * p.a_pitch + ch * 16;
   }
+  // LDS B row l holds weight row (output column) n0 + col_of(l), a
+  // permutation inside each wave's block chosen so that the MFMA column
+  // r16 of block n of a wave is column 4 r16 + n (gate/up: 64 columns per
+  // wave, blocks 0-3 gate and 4-7 the up rows of the same columns) or 8 r16
+  // + n (down: 128 columns per wave): a lane then holds 4 or 8 consecutive
+  // output columns of each of its rows and stores them in one piece
+  auto col_of = [](int l) {
+    return SWIGLU ? (l & ~63) + ((l & 15) << 2) + ((l >> 4) & 3)
+                  : (l & ~127) + ((l & 15) << 3) + ((l >> 4) & 7);
+  };
   const uint8_t *bsrc[8];
   {
 #pragma unroll
     for (int hh = 0; hh < 8; ++hh) {
       const int row = wave * 64 + hh * 8 + (lane >> 3);
       const int ch = (lane & 7) ^ ((row >> 1) & 7);
-      const int n = n0 + (SWIGLU ? (row & (kBW / 2 - 1)) : row);
+      const int n = n0 + col_of(SWIGLU ? (row & (kBW / 2 - 1)) : row);
       const uint8_t *base = (SWIGLU && wave >= 2) ? B1 : B0;
       bsrc[hh] = base + static_cast<int64_t>(min(n, N - 1)) * krow + ch * 16;
     }
@@ -438,41 +448,34 @@ void prefill_gemm4_kernel(const GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // the repeated loads of the last stage may still be landing in LDS
+  // the repeated loads of the last stage may still be landing in LDS, which
+  // the next workgroup on this CU will own
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // every wave is done with the ring before the epilogue reuses it
 
-  // ---- epilogue: stage the bf16 tile in LDS, then whole 16-byte stores.
-  // acc[m][n][i]: row wr*128 + 16 m + 4 q + i, weight row block n, column r16.
-  uint16_t *o16 = reinterpret_cast<uint16_t *>(lds);
-  // staged rows padded by 16 bytes: the four rows a store touches (4 apart)
-  // then fall in different LDS banks
-  constexpr int OPITCH = BNO + 8;
+  // ---- epilogue, straight from the accumulators (no LDS staging):
+  // acc[m][n][i] is row wr*128 + 16 m + 4 q + i and column 4 r16 + n
+  // (gate/up, n < 4 gate and n + 4 up: 4 consecutive z columns, one 8-byte
+  // store) or 8 r16 + n (down: 8 consecutive y columns, one 16-byte store)
+  // of the wave's columns (see col_of)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int col0 = SWIGLU ? n0 + wc * 64 + r16 * 4 : n0 + wc * 128 + r16 * 8;
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wr * 128 + m * 16 + 4 * q + i;
-      if (SWIGLU) {
+      if (row >= rows || col0 >= N) continue;
+      uint8_t *dst = p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + col0 * 2;
+      if constexpr (SWIGLU) {
+        float z[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n)
-          o16[row * OPITCH + wc * 64 + n * 16 + r16] =
-              f32_to_bf16(silu_mul(acc[m][n][i], acc[m][n + 4][i]));
+        for (int n = 0; n < 4; ++n) z[n] = silu_mul(acc[m][n][i], acc[m][n + 4][i]);
+        *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
       } else {
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-          o16[row * OPITCH + wc * 128 + n * 16 + r16] = f32_to_bf16(acc[m][n][i]);
+        st16(dst, u32x4{pack_bf16x2(acc[m][0][i], acc[m][1][i]), pack_bf16x2(acc[m][2][i], acc[m][3][i]),
+                        pack_bf16x2(acc[m][4][i], acc[m][5][i]), pack_bf16x2(acc[m][6][i], acc[m][7][i])});
       }
     }
-  __syncthreads();
-  constexpr int CPR = BNO * 2 / 16;  // 16-byte pieces of data per staged row
-  const int vcpr = min(CPR, (N - n0) * 2 / 16);
-  for (int c = tid; c < kBM * CPR; c += 256) {
-    const int row = c / CPR, col = c % CPR;
-    if (row < rows && col < vcpr)
-      st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
-           ld16(lds + row * OPITCH * 2 + col * 16));
-  }
 }
 
 // the dynamic-LDS limit is a per-device attribute of each kernel
@@ -498,26 +501,17 @@ hipError_t set_lds_limit() {
   return set_lds_limit(prefill_gemm_kernel<MODE>, attr_set);
 }
 
-// dynamic LDS of the four-wave kernel: the two stage buffers, or the padded
-// output tile of the epilogue if that is larger (down: 256 x 264 bf16)
-template <int MODE>
-constexpr size_t lds4_bytes() {
-  constexpr size_t ring = kRing * kSlot;
-  constexpr size_t out = static_cast<size_t>(kBM) * ((MODE == kGateUp ? kBW / 2 : kBW) + 8) * 2;
-  return ring > out ? ring : out;
-}
-
 template <int MODE>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = MODE == kGateUp ? kBW / 2 : kBW;
   static std::atomic<bool> attr_set[64];
-  hipError_t e = set_lds_limit(prefill_gemm4_kernel<MODE>, attr_set, lds4_bytes<MODE>());
+  hipError_t e = set_lds_limit(prefill_gemm4_kernel<MODE>, attr_set);
   if (e != hipSuccess) return e;
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int ntn = (nmax + BNO - 1) / BNO;
   const int64_t grid = 8LL * ((a.tiles_ub + 7) / 8) * ntn;
   if (grid <= 0) return hipSuccess;
-  prefill_gemm4_kernel<MODE><<<static_cast<unsigned>(grid), 256, lds4_bytes<MODE>(), s>>>(a);
+  prefill_gemm4_kernel<MODE><<<static_cast<unsigned>(grid), 256, kRing * kSlot, s>>>(a);
   return hipGetLastError();
 }
 
