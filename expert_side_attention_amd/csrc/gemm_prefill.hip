@@ -20,9 +20,14 @@
 // the 16 rows one MFMA operand read touches per quarter wave hit 16
 // different 4-bank groups.
 //
-// Tile order: row tiles are dealt round-robin to the 8 XCDs (workgroup ids
-// go to XCDs round-robin) and all column tiles of a row tile run on one XCD,
-// close in time: the XCD's L2 serves the activation rows to all of them.
+// Tile order (workgroup ids go to the 8 XCDs round-robin): the eight-wave
+// kernel deals row tiles round-robin to the XCDs and runs all column tiles
+// of a row tile on one XCD, close in time, so the XCD's L2 serves the
+// activation rows to all of them.  The four-wave kernel deals windows of 4
+// consecutive row tiles x up to 8 column tiles (about one workgroup per CU
+// of an XCD) instead: in a window each activation stage is read by up to 8
+// CUs and each weight stage by up to 4 (consecutive row tiles mostly belong
+// to one expert), and the 8 XCDs work on 8 consecutive windows at a time.
 //
 // Two kernels share this layout.  The expert GEMMs run on four waves (one
 // per SIMD), each owning 128 rows x 128 weight rows as 8 x 8 tiles of
@@ -54,6 +59,20 @@ constexpr int kSlot = (kBM + kBW) * kStage;  // 64 KB
 // index is XOR-ed with (row / 2) % 8 (see the file comment)
 __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * kStage + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// Four-wave kernel tile order: windows of kWinR consecutive row tiles x cw
+// column tiles (column tiles split into ncg groups of at most kWinC), each
+// window on one XCD; ws = kWinR * cw workgroups per window
+constexpr int kWinR = 4;
+constexpr int kWinC = 32 / kWinR;
+struct TileWindows {
+  int ncg, cw, ws;
+};
+__host__ __device__ inline TileWindows tile_windows(int ntn) {
+  const int ncg = (ntn + kWinC - 1) / kWinC;
+  const int cw = (ntn + ncg - 1) / ncg;
+  return {ncg, cw, kWinR * cw};
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -281,11 +300,14 @@ void prefill_gemm4_kernel(const GemmArgs p) {
 
   const int nmax = p.N > p.Ns ? p.N : p.Ns;
   const int ntn = (nmax + BNO - 1) / BNO;
+  const TileWindows tw = tile_windows(ntn);
   const int L = blockIdx.x;
   const int j = L >> 3;
-  const int mt = (L & 7) + 8 * (j / ntn);
-  const int nt = j % ntn;
-  if (mt >= *p.num_tiles) return;
+  const int gw = (j / tw.ws) * 8 + (L & 7);  // window; consecutive windows on consecutive XCDs
+  const int u = j % tw.ws;
+  const int mt = (gw / tw.ncg) * kWinR + u % kWinR;
+  const int nt = (gw % tw.ncg) * tw.cw + u / kWinR;
+  if (mt >= *p.num_tiles || nt >= ntn) return;
   const Tile tile = p.tiles[mt];
   const bool shared = tile.group >= p.E;
   const int N = shared ? p.Ns : p.N;
@@ -509,7 +531,9 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int nmax = a.N > a.Ns ? a.N : a.Ns;
   const int ntn = (nmax + BNO - 1) / BNO;
-  const int64_t grid = 8LL * ((a.tiles_ub + 7) / 8) * ntn;
+  const TileWindows tw = tile_windows(ntn);
+  const int64_t windows = static_cast<int64_t>((a.tiles_ub + kWinR - 1) / kWinR) * tw.ncg;
+  const int64_t grid = 8LL * ((windows + 7) / 8) * tw.ws;
   if (grid <= 0) return hipSuccess;
   prefill_gemm4_kernel<MODE><<<static_cast<unsigned>(grid), 256, kRing * kSlot, s>>>(a);
   return hipGetLastError();
