@@ -418,14 +418,16 @@ void prefill_gemm4_kernel(const GemmArgs p) {
   // wave waits for its loads of stage s + 1 and meets the others at the
   // barrier, after which nothing reads stage s from LDS any more; K step 1
   // on set 1 while the sixteen loads of stage s + 2 go into stage s's
-  // buffer, one per four MFMAs, and set 0 is read from stage s + 1.  A load
-  // thus has about one stage to arrive.  The loop has no branches: the
+  // buffer, one per four MFMAs (the weight rows, which miss the L2 more
+  // often, before the activation rows), and set 0 is read from stage s + 1.
+  // A load thus has about one stage to arrive.  The loop has no branches: the
   // loads advance their own pointers and, past the last stage, repeat it
   // (about 32 branches per stage around conditional loads had cost ~8%).
   // Measured alternatives were slower:
-  // the loads packed into the first quarter or half of step 1, or the
-  // barrier 16 MFMAs before the end of step 0 (which also made the register
-  // allocator move accumulators between register files inside the loop).
+  // the loads packed into the first quarter or half of step 1, weight and
+  // activation loads alternating, or the barrier 16 MFMAs before the end of
+  // step 0 (which also made the register allocator move accumulators
+  // between register files inside the loop).
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) load(0, jj);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -465,7 +467,7 @@ void prefill_gemm4_kernel(const GemmArgs p) {
     for (int i = 0; i < 64; ++i) {
       const int m = i >> 3, n = i & 7;
       acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][m], fb[1][n], acc[m][n], 0, 0, 0);
-      if ((i & 3) == 0) load_next(s & 1, i >> 2, adv);
+      if ((i & 3) == 0) load_next(s & 1, ((i >> 2) + 8) & 15, adv);  // weight rows first
       if ((i & 1) == 1 && i < 32) read(s1, 0, i >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
