@@ -103,6 +103,11 @@ SMALL = [
     LayerShape("bf16_prefill_h384", T=520, h=384, E=4, k=2, I=256, S=1, Is=128, mode="bf16"),
     LayerShape("bf16_prefill_skew", T=1500, h=256, E=16, k=2, I=256, S=1, Is=256,
                mode="bf16", router="zipf"),
+    # compute-bound tiles whose column tiles split unevenly into the XCD tile
+    # windows: gate/up 9 column tiles (groups of 5 and 4; the shared expert's
+    # narrower I_s leaves 5), down 3
+    LayerShape("bf16_prefill_windows", T=1000, h=768, E=4, k=2, I=1152, S=1, Is=640,
+               mode="bf16"),
     # tiny layers, at most 16 tokens, also run as one launch (FUSED below)
     LayerShape("fused_bf16_shared", T=13, h=512, E=32, k=6, I=256, S=2, Is=128, mode="bf16"),
     LayerShape("fused_bf16_e512_k16", T=7, h=128, E=512, k=16, I=128, S=1, Is=256,
