@@ -13,7 +13,8 @@ Prints one JSON line.  Extra fields: "roofline" of the dominant kernel and
 
 Roofline: weight-streaming layers (one micro-batch) time the gate/up launch
 with HIP events on the forward's stream over the timed region, against the
-algorithmic bytes of the touched experts.  The two-micro-batch prefill layer
+algorithmic bytes of the touched experts; where gate/up and down run as one
+launch (bf16 decode regime), that launch, against the bytes of both.  The two-micro-batch prefill layer
 times its compute-bound gate/up launch (256-row tiles) with HIP events in a
 serial pass after the timed region (micro-batches back to back on one
 stream, so no other kernel shares the interval), against the unpadded flops
@@ -83,12 +84,15 @@ def work_model(s, counts):
     io = 2 * s.T * s.h * ab
     router = s.E * s.h * ab
     gate_up_bytes = touched * per_gu + sh_gu + s.T * s.h * ab
+    # gate/up and down in one launch: both GEMMs' weights and X
+    ffn_bytes = gate_up_bytes + touched * per_dn + sh_dn
     flops = (2 * s.T * s.k * 3 * s.h * s.I + 2 * s.T * s.S * 3 * s.h * s.Is
              + 2 * s.T * s.h * s.E)
     gate_up_flops = 2 * s.T * s.k * 2 * s.h * s.I + 2 * s.T * s.S * 2 * s.h * s.Is
     return {
         "touched_experts": touched,
         "gate_up_bytes": gate_up_bytes,
+        "ffn_bytes": ffn_bytes,
         "gate_up_flops": gate_up_flops,
         "forward_bytes": touched * (per_gu + per_dn) + sh_gu + sh_dn + io + router,
         "forward_flops": flops,
@@ -142,7 +146,8 @@ def work_model_microbatches(s, layers, xs):
         if tot is None:
             tot = dict(m)
         else:
-            for kk in ("gate_up_bytes", "gate_up_flops", "forward_bytes", "forward_flops"):
+            for kk in ("gate_up_bytes", "ffn_bytes", "gate_up_flops", "forward_bytes",
+                       "forward_flops"):
                 tot[kk] += m[kk]
             tot["touched_experts"] = max(tot["touched_experts"], m["touched_experts"])
     tot["gate_up_big_flops"] = big_flops
@@ -270,6 +275,9 @@ def main():
     ap.add_argument("--single-launch", action="store_true",
                     help="run forwards of at most 16 tokens of a tiny layer as one "
                          "cooperative launch (the layer's single_launch option)")
+    ap.add_argument("--split-gemms", action="store_true",
+                    help="one launch per weight-streaming GEMM (the layer's split_gemms "
+                         "option; by default a bf16 decode layer runs both in one launch)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (profiler calibration)")
     ap.add_argument("--pipeline", action="store_true",
@@ -305,7 +313,8 @@ def main():
     log(f"[bench] building {shape.name} on {dev}")
     nmb = shape.micro_batches
     mbT = shape.T // nmb
-    layer = build_layer(syn, dev, max_tokens=mbT, single_launch=args.single_launch)
+    layer = build_layer(syn, dev, max_tokens=mbT, single_launch=args.single_launch,
+                        split_gemms=args.split_gemms)
     layers = [layer] + [layer.sibling() for _ in range(nmb - 1)]
     x = hidden_tensor(syn, dev)
     xs = [x[i * mbT:(i + 1) * mbT] for i in range(nmb)]
@@ -325,17 +334,18 @@ def main():
     for li in layers:
         li.profile_read()  # reset
 
-    # timed region: K steps; HIP events around the gate/up GEMM launches,
-    # recorded on the stream each forward runs on
+    # timed region: K steps; HIP events around the gate/up GEMM launches (or
+    # the single launch of gate/up and down), recorded on the stream each
+    # forward runs on
     for li in layers:
-        li.profile_enable(["gate_up", "single"])
+        li.profile_enable(["gate_up", "single", "ffn"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gu_ms = gu_n = one_ms = one_n = 0
+    gu_ms = gu_n = one_ms = one_n = ffn_ms = ffn_n = 0
     for li in layers:
         prof = li.profile_read()
         li.profile_enable([])
@@ -343,10 +353,14 @@ def main():
         gu_n += prof["gate_up"][1]
         one_ms += prof["single"][0]
         one_n += prof["single"][1]
+        ffn_ms += prof["ffn"][0]
+        ffn_n += prof["ffn"][1]
     ms_step = (t1 - t0) * 1e3 / args.steps
     gu_avg = gu_ms / max(gu_n, 1)
     # tiny layers run the whole forward as one launch
     one_avg = one_ms / one_n if one_n else None
+    # bf16 decode-regime layers run gate/up and down as one launch
+    ffn_avg = ffn_ms / ffn_n if ffn_n else None
 
     # two micro-batches: the dominant (compute-bound gate/up) launch timed in
     # a serial pass, so that no kernel of the other stream shares its
@@ -370,7 +384,7 @@ def main():
 
     # untimed breakdown of all stages, one micro-batch at a time
     all_stages = ["router", "dispatch", "quant", "gate_up", "down", "combine", "gate_up_big",
-                  "down_big", "single"]
+                  "down_big", "single", "ffn"]
     stage_tot = {}
     for li in layers:
         li.profile_enable(all_stages)
@@ -425,12 +439,19 @@ def main():
     ridge = MFMA_PEAK_TFLOPS[shape.mode] * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "mfma" if ai > ridge else "hbm"
     gu_launch_bytes = model["gate_up_bytes"] / nmb
+    kernel_name = "gate_up grouped GEMM + SwiGLU (weight streaming)"
+    tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{shape.name}.json")
     if one_avg is not None:
         # the single launch is the whole forward: its bytes are the forward's
         gu_launch_bytes, gu_avg = model["forward_bytes"], one_avg
+        kernel_name = "single-launch forward (fused_small_kernel)"
+    elif ffn_avg is not None:
+        gu_launch_bytes, gu_avg = model["ffn_bytes"] / nmb, ffn_avg
+        kernel_name = ("gate/up + SwiGLU and down grouped GEMMs, one launch "
+                       "(weight streaming, stream_ffn_kernel)")
+        tfile = os.path.join(ROOT, "profiles", f"traffic_ffn_{shape.name}.json")
     achieved = gu_launch_bytes / (gu_avg * 1e-3) / 1e9
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"traffic_gate_up_{shape.name}.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
             t = json.load(f)
@@ -439,8 +460,7 @@ def main():
     res_hash = kernel_source_hash()
     if bound == "hbm":
         roofline = {"bound": "hbm",
-                    "kernel": ("single-launch forward (fused_small_kernel)" if one_avg is not None
-                               else "gate_up grouped GEMM + SwiGLU (weight streaming)"),
+                    "kernel": kernel_name,
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "avg_launch_ms": round(gu_avg, 5),
@@ -481,7 +501,8 @@ def main():
         "config": {"workload": shape.name, "T": shape.T, "h": shape.h, "E": shape.E,
                    "k": shape.k, "I": shape.I, "S": shape.S, "Is": shape.Is,
                    "mode": shape.mode, "seed": args.seed,
-                   "single_launch": bool(args.single_launch)},
+                   "single_launch": bool(args.single_launch),
+                   "split_gemms": bool(args.split_gemms)},
         "roofline": roofline,
         "forward": {"hbm_gbs": round(fwd_gbs, 1), "hbm_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
                     "bytes": int(model["forward_bytes"]),

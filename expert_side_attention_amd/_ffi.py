@@ -15,13 +15,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libafd_ffn.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "afd_ffn.h")
 
-AFD_FFN_ABI_VERSION = 2
+AFD_FFN_ABI_VERSION = 3
 AFD_OK, AFD_ERR_INVALID_ARG, AFD_ERR_UNSUPPORTED = 0, 1, 2
 AFD_ERR_CAPACITY, AFD_ERR_OUT_OF_MEMORY, AFD_ERR_HIP = 3, 4, 5
 AFD_MODE_F32, AFD_MODE_BF16, AFD_MODE_W8A8_E4M3 = 0, 1, 2
 AFD_FFN_STATIC_SCRATCH_BYTES = 128 << 20
 STAGES = ("router", "dispatch", "quant", "gate_up", "down", "combine", "gate_up_big",
-          "down_big", "single")
+          "down_big", "single", "ffn")
 STAGE_INDEX = {n: i for i, n in enumerate(STAGES)}
 
 _STATUS_NAMES = {0: "AFD_OK", 1: "AFD_ERR_INVALID_ARG", 2: "AFD_ERR_UNSUPPORTED",
@@ -40,7 +40,7 @@ class afd_ffn_config(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("num_shared", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32), ("has_router_bias", ctypes.c_int32),
-                ("single_launch", ctypes.c_int32)]
+                ("single_launch", ctypes.c_int32), ("split_gemms", ctypes.c_int32)]
 
 
 class afd_ffn_weights(ctypes.Structure):

@@ -58,6 +58,8 @@ struct afd_ffn_handle {
   int tiles_cap, big_cap;
   void *ws;
   size_t ws_bytes;
+  // counters: the two GEMMs' work counters, then one completion counter per
+  // small tile (the single launch of both weight-streaming GEMMs)
   int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *num_big, *counters;
   int32_t *dispatch_scratch;
   float *topk_w, *logits;
@@ -126,6 +128,8 @@ int validate_config(const afd_ffn_config *c) {
     return fail(AFD_ERR_INVALID_ARG, "has_router_bias must be 0 or 1");
   if (c->single_launch != 0 && c->single_launch != 1)
     return fail(AFD_ERR_INVALID_ARG, "single_launch must be 0 or 1");
+  if (c->split_gemms != 0 && c->split_gemms != 1)
+    return fail(AFD_ERR_INVALID_ARG, "split_gemms must be 0 or 1");
   return AFD_OK;
 }
 
@@ -201,7 +205,7 @@ size_t layout_workspace(afd_ffn_handle *h, int64_t T, char *base) {
   add(&h->offsets, sizeof(int32_t) * (E + 1));
   add(&h->num_tiles, sizeof(int32_t));
   add(&h->num_big, sizeof(int32_t));
-  add(&h->counters, 2 * sizeof(int32_t));
+  add(&h->counters, (2 + static_cast<size_t>(h->tiles_cap)) * sizeof(int32_t));
   add(&h->dispatch_scratch, sizeof(int32_t) * 2 * afd::dispatch_blocks(static_cast<int>(T)) * E);
   add(&h->logits, sizeof(float) * static_cast<size_t>(afd::router_logit_floats(
                                       static_cast<int>(T), c.hidden, static_cast<int>(E))));
@@ -407,10 +411,19 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   if (e != hipSuccess) return hip_fail(e, "router launch");
 
   const afd::GemmPlan plan = afd::gemm_plan(h->elem, Ti, k, E);
+  // decode-regime bf16 layers: both weight-streaming GEMMs in one launch
+  const bool ffn_one_launch =
+      c.split_gemms == 0 && plan.small_kernel == afd::GemmKernel::Stream &&
+      plan.tiles.bm_big == 0 &&
+      afd::stream_ffn_supported(h->elem, plan.tiles.bm_small, hd, c.inter,
+                                S > 0 ? c.shared_inter : c.inter);
+  const int small_ub =
+      static_cast<int>(tiles_upper_bound(T, k, E, S, plan.tiles.bm_small));
   ev = prof_begin(h, AFD_STAGE_DISPATCH, s);
   e = afd::launch_dispatch(h->ids, Ti, k, E, S, plan.tiles, h->counts, h->offsets, h->perm,
                            h->slot_row, h->tiles, h->num_tiles, h->tiles_big, h->num_big,
-                           h->counters, 2, h->dispatch_scratch, s);
+                           h->counters, ffn_one_launch ? 2 + small_ub : 2,
+                           h->dispatch_scratch, s);
   prof_end(h, ev, s);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
 
@@ -462,10 +475,12 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
     g.C = reinterpret_cast<uint8_t *>(h->z32);
     g.c_pitch = static_cast<int64_t>(h->zpitch) * 4;
   }
-  ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
-  e = launch_gemms(h, afd::GemmKind::GateUp, plan, g, T, s);
-  prof_end(h, ev, s);
-  if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
+  if (!ffn_one_launch) {
+    ev = prof_begin(h, AFD_STAGE_GATE_UP, s);
+    e = launch_gemms(h, afd::GemmKind::GateUp, plan, g, T, s);
+    prof_end(h, ev, s);
+    if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
+  }
   if (z_fp32) {
     ev = prof_begin(h, AFD_STAGE_QUANT, s);
     const int64_t R = static_cast<int64_t>(Tk) + static_cast<int64_t>(S) * Ti;
@@ -505,10 +520,21 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   d.c_pitch = static_cast<int64_t>(hd) * yes;
   d.c_scale = nullptr;
   d.work_counter = h->counters + 1;
-  ev = prof_begin(h, AFD_STAGE_DOWN, s);
-  e = launch_gemms(h, afd::GemmKind::Down, plan, d, T, s);
-  prof_end(h, ev, s);
-  if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
+  if (ffn_one_launch) {
+    // one work counter (the gate/up one) for the items of both GEMMs
+    g.tiles = d.tiles = h->tiles;
+    g.num_tiles = d.num_tiles = h->num_tiles;
+    g.tiles_ub = d.tiles_ub = small_ub;
+    ev = prof_begin(h, AFD_STAGE_FFN, s);
+    e = afd::launch_ffn_stream(g, d, h->counters + 2, s);
+    prof_end(h, ev, s);
+    if (e != hipSuccess) return hip_fail(e, "gate/up + down GEMM launch");
+  } else {
+    ev = prof_begin(h, AFD_STAGE_DOWN, s);
+    e = launch_gemms(h, afd::GemmKind::Down, plan, d, T, s);
+    prof_end(h, ev, s);
+    if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
+  }
 
   ev = prof_begin(h, AFD_STAGE_COMBINE, s);
   e = afd::launch_combine(h->elem == 0, h->y, h->slot_row, h->topk_w, Ti, k, S, hd, out, s);

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_kernel(
   }
   if (tid == 0) offsets[E] = total;
   build_tiles(T, k, E, S, tp, c, off, wsum, tiles_s, num_s, tiles_b, num_b);
-  if (tid < ncounters) counters[tid] = 0;
+  for (int i = tid; i < ncounters; i += kThreads) counters[i] = 0;
   __syncthreads();
 
   // 3. stable scatter, 1024 tokens per pass
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(
   }
   if (tid == 0) offsets[E] = total;
   build_tiles(T, k, E, S, tp, c, off, wsum, tiles_s, num_s, tiles_b, num_b);
-  if (tid < ncounters) counters[tid] = 0;
+  for (int i = tid; i < ncounters; i += kThreads) counters[i] = 0;
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(

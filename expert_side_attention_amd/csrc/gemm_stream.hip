@@ -56,11 +56,15 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
-template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU>
+// WIDE (bf16 down only): an item covers two blocks of BN output columns,
+// held like the gate and up blocks of a gate/up item (two weight-row blocks
+// per wave, one staged activation tile for both).
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU, bool WIDE = false>
 struct StreamCfg {
   static constexpr int kThreads = WAVES * 64;
-  static constexpr int NMAT = SWIGLU ? 2 : 1;
+  static constexpr int NMAT = SWIGLU || WIDE ? 2 : 1;
   static constexpr int BN = 16 * WAVES;       // columns per matrix per item
+  static constexpr int ICOLS = WIDE ? 2 * BN : BN;  // output columns per item
   static constexpr int MB = BM / 16;
   static constexpr int NPR = SS / 128;        // 128-byte K pieces per row per super-stage
   static constexpr int APITCH = SS + 16;      // LDS row pitch of the A stage
@@ -72,55 +76,100 @@ struct StreamCfg {
   static constexpr int LDS_A = 2 * BM * APITCH;
   // epilogue staging: BM rows x BN columns of the output element
   static constexpr int OUT_ES = FP8 && SWIGLU ? 4 : 2;  // fp32 z (W8A8) or bf16
-  static constexpr int LDS_OUT = BM * BN * OUT_ES;
+  static constexpr int LDS_OUT = BM * ICOLS * OUT_ES;
   static constexpr int LDS = LDS_A > LDS_OUT ? LDS_A : LDS_OUT;
+  // fp8: activation scale x weight block scale, [buffer][matrix][K block][row]
+  using SAs = float[2][NMAT][FP8 ? KB : 1][FP8 ? BM : 4];
   static_assert(BM % 16 == 0 && SS % 128 == 0, "shape");
   static_assert(kThreads % CPR == 0 && BM % RPP == 0, "A staging passes");
   static_assert(!FP8 || 128 % BN == 0, "fp8: an item lies inside one weight scale block row");
   static_assert(!FP8 || BM * KB <= kThreads, "fp8: one activation scale per thread");
+  static_assert(!WIDE || (!SWIGLU && !FP8), "wide items: bf16 down GEMM only");
 };
+
+// Synchronisation of an item with the other GEMM of the same forward, for
+// the single launch that runs both weight-streaming GEMMs (gate/up items
+// first, then down items, from one work counter):
+//  kNoSync: the GEMM runs on its own (one launch per GEMM);
+//  kSignal: a gate/up item writes its z columns through to memory
+//           (agent-scope stores) and then counts itself finished in the
+//           tile's counter;
+//  kWait:   a down item waits until every gate/up item of its tile has
+//           counted itself (a bounded wait) before it reads z.
+enum { kNoSync = 0, kSignal = 1, kWait = 2 };
+
+// Polls of a tile counter before a down item gives up waiting (about a
+// quarter of a second; a legitimate wait is one gate/up item, a few hundred
+// microseconds).  Every gate/up item is claimed before any down item, by a
+// workgroup that is running and waits on nothing, so the bound is never
+// reached; it only keeps a defect from hanging the device.
+constexpr int kTileWaitPolls = 1 << 18;
+
+// 16-byte store that is visible to every CU of the device once the store
+// counter has drained (two agent-scope 8-byte stores).
+__device__ __forceinline__ void st16_agent(uint8_t *dst, u32x4 v) {
+  uint64_t *d = reinterpret_cast<uint64_t *>(dst);
+  __hip_atomic_store(d, static_cast<uint64_t>(v[0]) | (static_cast<uint64_t>(v[1]) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, static_cast<uint64_t>(v[2]) | (static_cast<uint64_t>(v[3]) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // K (in bytes per row) must be a multiple of SS for every group; the
 // launcher picks an instantiation that satisfies this, so the main loop has
 // no partial super-stage and no per-load guard.
 // AD: how many super-stages ahead the activation rows are loaded (1 or 2).
-template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU, int AD>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void stream_gemm_kernel(const GemmArgs p) {
-  using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU>;
+// One work item (row tile x BN columns) of the weight-streaming GEMM.
+// tile_done / gu_bn: the tile counters and the gate/up item width of the
+// single launch (SYNC != kNoSync).
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU, int AD, int SYNC, int GU_BN = 0,
+          bool WIDE = false>
+__device__ __forceinline__ void stream_item(
+    const GemmArgs &p, const int item, uint8_t *lds,
+    typename StreamCfg<EL, WAVES, BM, SS, SWIGLU, WIDE>::SAs &sAs, int32_t *tile_done) {
+  using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU, WIDE>;
+  constexpr int ICOLS = C::ICOLS;
   constexpr int NMAT = C::NMAT, BN = C::BN, MB = C::MB, NPR = C::NPR;
   constexpr int APITCH = C::APITCH, CPR = C::CPR, RPP = C::RPP, RA = C::RA, KB = C::KB;
-
-  __shared__ __align__(16) uint8_t lds[C::LDS];
   static_assert(AD == 1 || AD == 2, "activation prefetch distance");
-  // fp8: activation scale x weight block scale, [buffer][matrix][K block][row]
-  __shared__ __align__(16) float sAs[2][NMAT][C::FP8 ? KB : 1][C::FP8 ? BM : 4];
-  __shared__ int s_item;
+  static_assert(SYNC == kNoSync || (!C::FP8 && (SYNC != kSignal || SWIGLU) &&
+                                    (SYNC != kWait || (!SWIGLU && GU_BN > 0))),
+                "the single launch of both GEMMs is bf16: gate/up signals, down waits");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const int nmax = p.N > p.Ns ? p.N : p.Ns;
-  const int ntn = nmax / BN;
-  const int total = *p.num_tiles * ntn;
+  const int ntn = nmax / ICOLS;
   const int acol = tid % CPR, arow0 = tid / CPR;  // this thread's A chunk column, first row
   constexpr int ES = C::FP8 ? 1 : 2;
 
-  for (;;) {
-    __syncthreads();  // every thread has read the previous s_item
-    if (tid == 0) s_item = atomicAdd(p.work_counter, 1);
-    __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= total) break;
-    const Tile tile = p.tiles[item / ntn];
+  {
+    const int ti = item / ntn;
+    const Tile tile = p.tiles[ti];
     const int nt = item % ntn;
     const bool shared = tile.group >= p.E;
     const int N = shared ? p.Ns : p.N;
     const int K = shared ? p.Ks : p.K;
-    const int n0 = nt * BN;
-    if (n0 >= N) continue;  // uniform over the workgroup
+    const int n0 = nt * ICOLS;
+    if (n0 >= N) return;  // uniform over the workgroup
     const int g = shared ? tile.group - p.E : tile.group;
     const int rows = tile.rows;
     const int64_t krow = static_cast<int64_t>(K) * ES;
     const int nss = static_cast<int>(krow / SS);
+
+    if constexpr (SYNC == kWait) {
+      // z of this tile is complete once its K / GU_BN gate/up items (the
+      // down GEMM's K is the gate/up GEMM's N) have counted themselves
+      if (tid == 0) {
+        const int need = K / GU_BN;
+        for (int poll = 0; poll < kTileWaitPolls; ++poll) {
+          if (__hip_atomic_load(tile_done + ti, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need)
+            break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+    }
 
     // A rows this thread stages; rows past the tile's end repeat its first
     // row (they only feed output rows that are never stored)
@@ -158,6 +207,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
         if constexpr (SWIGLU) {
           const uint8_t *b1 = (shared ? p.sb1 : p.b1) + g * mat;
           bptr[NMAT - 1] = b1 + static_cast<int64_t>(n0 + wave * 16 + r16) * krow + q * 16;
+        } else if constexpr (WIDE) {
+          bptr[1] = b0 + static_cast<int64_t>(n0 + BN + wave * 16 + r16) * krow + q * 16;
         }
       }
       const float *bsc[NMAT] = {};
@@ -395,16 +446,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int row = b * 16 + q * 4 + i;
-            const float v = SWIGLU ? silu_mul(acc[0][b][i], acc[NMAT - 1][b][i]) : acc[0][b][i];
-            o16[row * BN + wave * 16 + r16] = f32_to_bf16(v);
+            if constexpr (WIDE) {
+              o16[row * ICOLS + wave * 16 + r16] = f32_to_bf16(acc[0][b][i]);
+              o16[row * ICOLS + BN + wave * 16 + r16] = f32_to_bf16(acc[1][b][i]);
+            } else {
+              const float v = SWIGLU ? silu_mul(acc[0][b][i], acc[NMAT - 1][b][i]) : acc[0][b][i];
+              o16[row * BN + wave * 16 + r16] = f32_to_bf16(v);
+            }
           }
         __syncthreads();
-        constexpr int PIECES = BM * BN * 2 / 16;
+        constexpr int PIECES = BM * ICOLS * 2 / 16;
         for (int c = tid; c < PIECES; c += C::kThreads) {
-          const int row = c / (BN * 2 / 16), col = c % (BN * 2 / 16);
-          if (row < rows)
-            st16(p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16,
-                 ld16(lds + row * BN * 2 + col * 16));
+          const int row = c / (ICOLS * 2 / 16), col = c % (ICOLS * 2 / 16);
+          if (row < rows) {
+            uint8_t *dst = p.C + static_cast<int64_t>(tile.row0 + row) * p.c_pitch + n0 * 2 + col * 16;
+            if constexpr (SYNC == kSignal)
+              st16_agent(dst, ld16(lds + row * ICOLS * 2 + col * 16));
+            else
+              st16(dst, ld16(lds + row * ICOLS * 2 + col * 16));
+          }
         }
       }
     };
@@ -423,7 +483,68 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
       body(Half{}, Two{});
     else
       body(Full{}, std::integral_constant<int, AD>{});
+    if constexpr (SYNC == kSignal) {
+      // every thread's z stores have reached the device-wide point of
+      // coherence before the tile counter says so
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(tile_done + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // the next item's first barrier orders these LDS reads before reuse
+  }
+}
+
+template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU, int AD>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void stream_gemm_kernel(const GemmArgs p) {
+  using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU>;
+  __shared__ __align__(16) uint8_t lds[C::LDS];
+  // fp8: activation scale x weight block scale, [buffer][matrix][K block][row]
+  __shared__ __align__(16) typename C::SAs sAs;
+  __shared__ int s_item;
+  const int total = *p.num_tiles * ((p.N > p.Ns ? p.N : p.Ns) / C::BN);
+  for (;;) {
+    __syncthreads();  // every thread has read the previous s_item
+    if (threadIdx.x == 0) s_item = atomicAdd(p.work_counter, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= total) break;
+    stream_item<EL, WAVES, BM, SS, SWIGLU, AD, kNoSync>(p, item, lds, sAs, nullptr);
+  }
+}
+
+// Both weight-streaming GEMMs of a bf16 decode forward in one persistent
+// launch: the workgroups claim the gate/up items (8 waves x 64 rows x 128 z
+// columns) and then the down items (8 waves x 64 rows x 128 output columns,
+// or with WIDE two 128-column weight blocks per item, so a row tile's z rows
+// are staged half as often per weight byte) from one counter, so the last
+// gate/up items run beside the first down items instead of leaving CUs idle
+// before a second launch.  A down item starts
+// once every gate/up item of its row tile has finished (tile counters,
+// zeroed by the dispatch kernel).  Per item the arithmetic is that of the
+// separate launches, so the results are bitwise the same.
+template <int SSG, int SSD, bool WIDE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void stream_ffn_kernel(
+    const GemmArgs gu, const GemmArgs dn, int32_t *tile_done) {
+  using CG = StreamCfg<Elem::BF16, 8, 64, SSG, true>;
+  using CD = StreamCfg<Elem::BF16, 8, 64, SSD, false, WIDE>;
+  constexpr int kLds = CG::LDS > CD::LDS ? CG::LDS : CD::LDS;
+  __shared__ __align__(16) uint8_t lds[kLds];
+  __shared__ __align__(16) typename CG::SAs sAsG;
+  __shared__ __align__(16) typename CD::SAs sAsD;
+  __shared__ int s_item;
+  const int n_gu = *gu.num_tiles * ((gu.N > gu.Ns ? gu.N : gu.Ns) / CG::BN);
+  const int n_all = n_gu + *dn.num_tiles * ((dn.N > dn.Ns ? dn.N : dn.Ns) / CD::ICOLS);
+  for (;;) {
+    __syncthreads();  // every thread has read the previous s_item
+    if (threadIdx.x == 0) s_item = atomicAdd(gu.work_counter, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= n_all) break;
+    if (item < n_gu)
+      stream_item<Elem::BF16, 8, 64, SSG, true, 1, kSignal>(gu, item, lds, sAsG, tile_done);
+    else
+      stream_item<Elem::BF16, 8, 64, SSD, false, 2, kWait, CG::BN, WIDE>(dn, item - n_gu, lds,
+                                                                           sAsD, tile_done);
   }
 }
 
@@ -459,9 +580,80 @@ hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Down items 256 columns wide when there are few per resident workgroup
+// (fewer than this many 128-column items): there each item's start is a
+// large share of its time (decode h4096 layer: 0.502 against 0.521 ms per
+// forward with 128-column items; DeepSeek-V3 EP8 shard 0.522 against
+// 0.537); with many items the narrow ones measured 1% faster (DeepSeek-V3
+// decode).  Both widths give the same bits.
+constexpr int kWideBelowItemsPerSlot = 32;
+
+template <int SSG, int SSD, bool WIDE>
+hipError_t launch_ffn(const GemmArgs &gu, const GemmArgs &dn, int32_t *tile_done, hipStream_t s,
+                      int slots) {
+  const int64_t items =
+      static_cast<int64_t>(gu.tiles_ub) * ((gu.N > gu.Ns ? gu.N : gu.Ns) / 128 +
+                                           (dn.N > dn.Ns ? dn.N : dn.Ns) / (WIDE ? 256 : 128));
+  int64_t grid = slots;
+  if (items < grid) grid = items;
+  if (grid <= 0) return hipSuccess;
+  stream_ffn_kernel<SSG, SSD, WIDE><<<static_cast<unsigned>(grid), 512, 0, s>>>(gu, dn, tile_done);
+  return hipGetLastError();
+}
+
+// resident workgroups of the single launch on the current device (every
+// instantiation has the same block size and holds one workgroup per CU)
+hipError_t ffn_slots(int *slots_out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> resident[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int slots = resident[dev].load(std::memory_order_relaxed);
+  if (slots <= 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void *>(stream_ffn_kernel<512, 512, true>), 512, 0);
+    if (e != hipSuccess || per_cu < 1) per_cu = 1;
+    slots = cus * per_cu;
+    resident[dev].store(slots, std::memory_order_relaxed);
+  }
+  *slots_out = slots;
+  return hipSuccess;
+}
+
 }  // namespace
 
 bool stream_gate_up_writes_fp8(int elem, int bm) { return elem == 2 && bm == 128; }
+
+bool stream_ffn_supported(int elem, int bm, int hidden, int inter, int shared_inter) {
+  // gate/up items of 128 z columns (I, I_s multiples of 128) and down items
+  // of 256 output columns; gate/up stages 512 bytes of K
+  return elem == 1 && bm == 64 && hidden % 256 == 0 && inter % 128 == 0 &&
+         shared_inter % 128 == 0;
+}
+
+hipError_t launch_ffn_stream(const GemmArgs &gu, const GemmArgs &dn, int32_t *tile_done,
+                             hipStream_t s) {
+  if (!stream_ffn_supported(1, 64, gu.K, gu.N, gu.Ns) || gu.K != gu.Ks || dn.N != gu.K ||
+      dn.K != gu.N || dn.Ks != gu.Ns || gu.tiles != dn.tiles || gu.num_tiles != dn.num_tiles)
+    return hipErrorInvalidValue;
+  int slots = 0;
+  hipError_t e = ffn_slots(&slots);
+  if (e != hipSuccess) return e;
+  const int64_t narrow = static_cast<int64_t>(gu.tiles_ub) * ((dn.N > dn.Ns ? dn.N : dn.Ns) / 128);
+  const bool wide = narrow < static_cast<int64_t>(kWideBelowItemsPerSlot) * slots;
+  // down: 512-byte stages where every K allows them
+  const bool ss512 = dn.K % 256 == 0 && dn.Ks % 256 == 0;
+  if (wide)
+    return ss512 ? launch_ffn<512, 512, true>(gu, dn, tile_done, s, slots)
+                 : launch_ffn<512, 256, true>(gu, dn, tile_done, s, slots);
+  return ss512 ? launch_ffn<512, 512, false>(gu, dn, tile_done, s, slots)
+               : launch_ffn<512, 256, false>(gu, dn, tile_done, s, slots);
+}
 
 hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
                               hipStream_t s) {

@@ -45,7 +45,8 @@ struct TilePlan {
 
 // Histogram, scan and stable scatter of the (token, slot) pairs, and the
 // two GEMM tile lists (routed experts, then the S shared groups).  Also
-// zeroes `counters[0..ncounters)` (the GEMMs' work counters).
+// zeroes `counters[0..ncounters)` (the GEMMs' work counters and, for the
+// single launch of both weight-streaming GEMMs, the tile counters).
 // block_scratch: 2 * dispatch_blocks(T) * E int32 (used when T > 1024).
 int dispatch_blocks(int T);
 hipError_t launch_dispatch(const int32_t *ids, int T, int k, int E, int S,
@@ -114,6 +115,14 @@ hipError_t launch_gemm(GemmKind kind, int elem, int bm, const GemmArgs &a,
 bool stream_gate_up_writes_fp8(int elem, int bm);
 hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,
                               hipStream_t s);
+// Both weight-streaming GEMMs (gate/up, then down) of a bf16 forward with
+// 64-row tiles in one persistent launch.  gu and dn use the same tile list;
+// tile_done holds one counter per tile of that list, zeroed before the
+// launch (the dispatch kernel does it).  stream_ffn_supported tells whether
+// a layer's shapes allow it.
+bool stream_ffn_supported(int elem, int bm, int hidden, int inter, int shared_inter);
+hipError_t launch_ffn_stream(const GemmArgs &gu, const GemmArgs &dn, int32_t *tile_done,
+                             hipStream_t s);
 // Compute-bound kernel (bf16, bm 256).
 hipError_t launch_gemm_prefill(GemmKind kind, const GemmArgs &a, hipStream_t s);
 // Router logits of long batches on the compute-bound kernel: partials[p][t][e]

@@ -73,7 +73,8 @@ class FfnLayer:
                  router_w, gate_w, up_w, down_w, router_b=None,
                  gate_s=None, up_s=None, down_s=None, num_shared=0,
                  shared_inter=0, sh_gate_w=None, sh_up_w=None, sh_down_w=None,
-                 sh_gate_s=None, sh_up_s=None, sh_down_s=None, single_launch=False):
+                 sh_gate_s=None, sh_up_s=None, sh_down_s=None, single_launch=False,
+                 split_gemms=False):
         if mode not in _MODES:
             raise ValueError(f"mode must be one of {sorted(_MODES)}")
         self.mode = mode
@@ -110,8 +111,9 @@ class FfnLayer:
             abi_version=F.AFD_FFN_ABI_VERSION, mode=_MODES[mode], hidden=h,
             num_experts=E, top_k=top_k, inter=I, num_shared=S, shared_inter=Is,
             max_tokens=max_tokens, has_router_bias=int(router_b is not None),
-            single_launch=int(bool(single_launch)))
+            single_launch=int(bool(single_launch)), split_gemms=int(bool(split_gemms)))
         self.single_launch = bool(single_launch)
+        self.split_gemms = bool(split_gemms)
         w = F.afd_ffn_weights(*[_ptr(t) for t in self._keep])
         self._cfg, self._w = cfg, w
         with torch.cuda.device(dev):
@@ -127,7 +129,7 @@ class FfnLayer:
                         gate_s=k[5], up_s=k[6], down_s=k[7], num_shared=self.num_shared,
                         shared_inter=self.shared_inter, sh_gate_w=k[8], sh_up_w=k[9],
                         sh_down_w=k[10], sh_gate_s=k[11], sh_up_s=k[12], sh_down_s=k[13],
-                        single_launch=self.single_launch)
+                        single_launch=self.single_launch, split_gemms=self.split_gemms)
 
     def forward(self, hidden: torch.Tensor, out: torch.Tensor = None, stream=None,
                 trace: bool = False):

@@ -27,9 +27,11 @@ def hidden_tensor(syn: SyntheticLayer, device):
     return to_device(syn.hidden(), device, syn.shape.mode != "f32")
 
 
-def build_layer(syn: SyntheticLayer, device, max_tokens=None, threads=16, single_launch=False):
+def build_layer(syn: SyntheticLayer, device, max_tokens=None, threads=16, single_launch=False,
+                split_gemms=False):
     """FfnLayer holding the synthetic layer's weights on `device`
-    (single_launch: forwards of at most 16 tokens as one launch)."""
+    (single_launch: forwards of at most 16 tokens as one launch; split_gemms:
+    one launch per weight-streaming GEMM)."""
     s = syn.shape
     bf16 = s.mode != "f32"
     dt = torch.bfloat16 if bf16 else torch.float32
@@ -56,7 +58,8 @@ def build_layer(syn: SyntheticLayer, device, max_tokens=None, threads=16, single
     router_b = None if b is None else torch.from_numpy(b).to(device)
     kw = dict(mode=s.mode, hidden=h, num_experts=E, top_k=s.k, inter=I,
               max_tokens=max_tokens or s.T, router_w=router_w, router_b=router_b,
-              num_shared=s.S, shared_inter=s.Is, single_launch=single_launch)
+              num_shared=s.S, shared_inter=s.Is, single_launch=single_launch,
+              split_gemms=split_gemms)
     if s.mode == "w8a8":
         (gq, gs), (uq, us), (dq, ds) = (quantize_fp8_128x128(t) for t in (gate, up, down))
         kw.update(gate_w=gq, up_w=uq, down_w=dq, gate_s=gs, up_s=us, down_s=ds)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define AFD_FFN_ABI_VERSION 2u
+#define AFD_FFN_ABI_VERSION 3u
 
 typedef struct afd_ffn_handle afd_ffn_handle;
 typedef void *afd_stream_t; /* a hipStream_t */
@@ -94,6 +94,13 @@ typedef struct {
                              fp32 / bf16 layer (top_k <= 16, expert weights
                              <= 64 MiB) as one cooperative launch (outside
                              graph capture); 0: the kernel sequence          */
+  int32_t split_gemms;    /* 0: a bf16 layer in the decode regime (at most
+                             48 routed rows per expert on average, hidden a
+                             multiple of 256) runs its gate/up and down
+                             weight-streaming GEMMs as one launch, the down
+                             work of a row tile starting as soon as that
+                             tile's z is complete (same results); 1: always
+                             one launch per GEMM                             */
 } afd_ffn_config;
 
 /* Weight pointers (device, borrowed).  The experts are SwiGLU matrix
@@ -259,7 +266,9 @@ int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols,
  * launches of the gate/up and down stages (256-row tiles) are also timed
  * on their own under AFD_STAGE_GATE_UP_BIG and AFD_STAGE_DOWN_BIG; a forward
  * that runs as one launch (tiny layers, at most 16 tokens) is timed under
- * AFD_STAGE_SINGLE only.  Stage bits:                                                                    */
+ * AFD_STAGE_SINGLE only, and the single launch of both weight-streaming
+ * GEMMs (config split_gemms = 0) under AFD_STAGE_FFN (AFD_STAGE_GATE_UP and
+ * AFD_STAGE_DOWN then record nothing).  Stage bits:                                                                    */
 #define AFD_STAGE_ROUTER   0
 #define AFD_STAGE_DISPATCH 1
 #define AFD_STAGE_QUANT    2
@@ -269,7 +278,8 @@ int afd_quant_fp8_128x128(const void *w, int64_t rows, int64_t cols,
 #define AFD_STAGE_GATE_UP_BIG 6
 #define AFD_STAGE_DOWN_BIG 7
 #define AFD_STAGE_SINGLE   8  /* the single-launch forward of tiny layers */
-#define AFD_STAGE_COUNT    9
+#define AFD_STAGE_FFN      9  /* gate/up + down weight streaming, one launch */
+#define AFD_STAGE_COUNT    10
 int afd_ffn_profile_enable(afd_ffn_handle *h, uint32_t stage_mask);
 int afd_ffn_profile_read(afd_ffn_handle *h, double *ms /*[AFD_STAGE_COUNT]*/,
                          int64_t *launches /*[AFD_STAGE_COUNT]*/);

@@ -90,6 +90,7 @@ def _w(**kw):
     (dict(max_tokens=0), {}, F.AFD_ERR_INVALID_ARG, "max_tokens"),
     (dict(has_router_bias=1), {}, F.AFD_ERR_INVALID_ARG, "router_b"),
     (dict(single_launch=2), {}, F.AFD_ERR_INVALID_ARG, "single_launch"),
+    (dict(split_gemms=-1), {}, F.AFD_ERR_INVALID_ARG, "split_gemms"),
     ({}, dict(gate_w=None), F.AFD_ERR_INVALID_ARG, "gate_w"),
     (dict(mode=F.AFD_MODE_W8A8_E4M3), {}, F.AFD_ERR_INVALID_ARG, "gate_s"),
     (dict(num_shared=1, shared_inter=256), {}, F.AFD_ERR_INVALID_ARG, "sh_gate_w"),
