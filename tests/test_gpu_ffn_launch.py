@@ -27,6 +27,9 @@ SHAPES = [
     # column blocks, over 32 per CU of 256) for 128-column down items; the
     # layers above take 256-column ones
     LayerShape("ffn_narrow", T=1024, h=2048, E=512, k=8, I=128, S=1, Is=256, mode="bf16"),
+    # over 1024 tokens: the dispatch runs in blocks and its scan kernel zeroes
+    # the tile counters
+    LayerShape("ffn_blocks", T=2100, h=256, E=512, k=8, I=128, S=1, Is=128, mode="bf16"),
 ]
 
 
