@@ -241,7 +241,7 @@ def pipeline(args):
     M = 2
     syn = SyntheticLayer(shape.with_tokens(M * shape.T), seed=args.seed)
     log(f"[bench] pipeline: building {shape.name} x {M} micro-batches on {dev}")
-    ffn0 = build_layer(syn, dev, max_tokens=shape.T)
+    ffn0 = build_layer(syn, dev, max_tokens=shape.T, split_gemms=args.split_gemms)
     ffns = [ffn0, ffn0.sibling()]
     x = hidden_tensor(syn, dev)
     xs = [x[m * shape.T:(m + 1) * shape.T].contiguous() for m in range(M)]
@@ -256,6 +256,7 @@ def pipeline(args):
 
     out = {"pipeline": rounded(res),
            "config": {"workload": shape.name, "micro_batch_tokens": shape.T, "micro_batches": M,
+                      "split_gemms": bool(args.split_gemms),
                       "attention_stub": {"context": args.pipeline_context, "heads": 16, "d": 512,
                                          "kv_bytes_per_micro_batch": attn[0].kv_bytes()}},
            "data": "synthetic"}
@@ -275,6 +276,9 @@ def main():
     ap.add_argument("--single-launch", action="store_true",
                     help="run forwards of at most 16 tokens of a tiny layer as one "
                          "cooperative launch (the layer's single_launch option)")
+    ap.add_argument("--micro-batches", type=int, default=0, metavar="M",
+                    help="M micro-batches of the workload's micro-batch size, one HIP stream "
+                         "each (default: the workload's own count)")
     ap.add_argument("--split-gemms", action="store_true",
                     help="one launch per weight-streaming GEMM (the layer's split_gemms "
                          "option; by default a bf16 decode layer runs both in one launch)")
@@ -308,6 +312,12 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     shape = CONFIGS[args.workload]
+    if args.micro_batches:
+        if args.micro_batches < 1:
+            raise SystemExit("--micro-batches must be at least 1")
+        import dataclasses
+        shape = dataclasses.replace(shape, T=shape.T // shape.micro_batches * args.micro_batches,
+                                    micro_batches=args.micro_batches)
     syn = SyntheticLayer(shape, seed=args.seed)
     dev = "cuda:0"
     log(f"[bench] building {shape.name} on {dev}")
@@ -502,7 +512,7 @@ def main():
                    "k": shape.k, "I": shape.I, "S": shape.S, "Is": shape.Is,
                    "mode": shape.mode, "seed": args.seed,
                    "single_launch": bool(args.single_launch),
-                   "split_gemms": bool(args.split_gemms)},
+                   "split_gemms": bool(args.split_gemms), "micro_batches": nmb},
         "roofline": roofline,
         "forward": {"hbm_gbs": round(fwd_gbs, 1), "hbm_frac": round(fwd_gbs / HBM_PEAK_GBS, 4),
                     "bytes": int(model["forward_bytes"]),

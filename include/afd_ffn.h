@@ -99,8 +99,10 @@ typedef struct {
                              multiple of 256) runs its gate/up and down
                              weight-streaming GEMMs as one launch, the down
                              work of a row tile starting as soon as that
-                             tile's z is complete (same results); 1: always
-                             one launch per GEMM                             */
+                             tile's z is complete (same results; best for a
+                             GPU the FFN service has to itself); 1: always
+                             one launch per GEMM (better when other streams
+                             share the GPU, e.g. attention on the same chip) */
 } afd_ffn_config;
 
 /* Weight pointers (device, borrowed).  The experts are SwiGLU matrix
