@@ -53,7 +53,7 @@ class afd_ffn_weights(ctypes.Structure):
 class afd_ffn_trace(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "topk_ids", "topk_w", "counts", "offsets", "perm", "slot_row", "x_q",
-        "x_s", "logits", "z_q", "z_s", "num_tiles")]
+        "x_s", "logits", "z_q", "z_s", "num_tiles", "sync_timeouts")]
 
 
 _lib = None

@@ -58,8 +58,9 @@ struct afd_ffn_handle {
   int tiles_cap, big_cap;
   void *ws;
   size_t ws_bytes;
-  // counters: the two GEMMs' work counters, then one completion counter per
-  // small tile (the single launch of both weight-streaming GEMMs)
+  // counters: the two GEMMs' work counters, then the sync words of the
+  // single launch of both weight-streaming GEMMs (items that gave up waiting,
+  // then one completion counter per small tile)
   int32_t *ids, *counts, *offsets, *perm, *slot_row, *num_tiles, *num_big, *counters;
   int32_t *dispatch_scratch;
   float *topk_w, *logits;
@@ -205,7 +206,7 @@ size_t layout_workspace(afd_ffn_handle *h, int64_t T, char *base) {
   add(&h->offsets, sizeof(int32_t) * (E + 1));
   add(&h->num_tiles, sizeof(int32_t));
   add(&h->num_big, sizeof(int32_t));
-  add(&h->counters, (2 + static_cast<size_t>(h->tiles_cap)) * sizeof(int32_t));
+  add(&h->counters, (3 + static_cast<size_t>(h->tiles_cap)) * sizeof(int32_t));
   add(&h->dispatch_scratch, sizeof(int32_t) * 2 * afd::dispatch_blocks(static_cast<int>(T)) * E);
   add(&h->logits, sizeof(float) * static_cast<size_t>(afd::router_logit_floats(
                                       static_cast<int>(T), c.hidden, static_cast<int>(E))));
@@ -393,6 +394,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
       fa.slot_row = h->slot_row;
       fa.num_tiles = h->num_tiles;
       fa.num_big = h->num_big;
+      fa.sync_timeouts = h->counters + 2;
       fa.z = h->z;
       fa.out = out;
       ev = prof_begin(h, AFD_STAGE_SINGLE, s);
@@ -422,7 +424,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
   ev = prof_begin(h, AFD_STAGE_DISPATCH, s);
   e = afd::launch_dispatch(h->ids, Ti, k, E, S, plan.tiles, h->counts, h->offsets, h->perm,
                            h->slot_row, h->tiles, h->num_tiles, h->tiles_big, h->num_big,
-                           h->counters, ffn_one_launch ? 2 + small_ub : 2,
+                           h->counters, ffn_one_launch ? 3 + small_ub : 3,
                            h->dispatch_scratch, s);
   prof_end(h, ev, s);
   if (e != hipSuccess) return hip_fail(e, "dispatch launch");
@@ -526,7 +528,7 @@ static int forward_impl(afd_ffn_handle *h, const void *hidden, void *out, int64_
     g.num_tiles = d.num_tiles = h->num_tiles;
     g.tiles_ub = d.tiles_ub = small_ub;
     ev = prof_begin(h, AFD_STAGE_FFN, s);
-    e = afd::launch_ffn_stream(g, d, h->counters + 2, s);
+    e = afd::launch_ffn_stream(g, d, h->counters + 2, s);  // sync words
     prof_end(h, ev, s);
     if (e != hipSuccess) return hip_fail(e, "gate/up + down GEMM launch");
   } else {
@@ -576,6 +578,7 @@ int afd_ffn_forward_traced(afd_ffn_handle *h, const void *hidden, void *out, int
       {tr->z_s, h->zs, R * (h->zpitch / 128) * 4},
       {tr->num_tiles, h->num_tiles, 4},
       {tr->num_tiles ? tr->num_tiles + 1 : nullptr, h->num_big, 4},
+      {tr->sync_timeouts, h->counters + 2, 4},
   };
   for (auto &cp : cps) {
     if (!cp.dst) continue;

@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void fused_small_kernel(const FusedArgs a
     if (tid == 0) {
       a.num_tiles[0] = 0;
       a.num_big[0] = 0;
+      a.sync_timeouts[0] = 0;
     }
   }
 

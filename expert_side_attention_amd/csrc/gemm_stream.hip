@@ -96,13 +96,16 @@ struct StreamCfg {
 //           tile's counter;
 //  kWait:   a down item waits until every gate/up item of its tile has
 //           counted itself (a bounded wait) before it reads z.
+// The launch's sync words: sync[0] counts down items that gave up waiting,
+// sync[1 + t] is the counter of tile t.
 enum { kNoSync = 0, kSignal = 1, kWait = 2 };
 
 // Polls of a tile counter before a down item gives up waiting (about a
 // quarter of a second; a legitimate wait is one gate/up item, a few hundred
 // microseconds).  Every gate/up item is claimed before any down item, by a
 // workgroup that is running and waits on nothing, so the bound is never
-// reached; it only keeps a defect from hanging the device.
+// reached; it only keeps a defect from hanging the device, and such an item
+// is counted in sync[0], which the traced forward reports.
 constexpr int kTileWaitPolls = 1 << 18;
 
 // 16-byte store that is visible to every CU of the device once the store
@@ -120,13 +123,13 @@ __device__ __forceinline__ void st16_agent(uint8_t *dst, u32x4 v) {
 // no partial super-stage and no per-load guard.
 // AD: how many super-stages ahead the activation rows are loaded (1 or 2).
 // One work item (row tile x BN columns) of the weight-streaming GEMM.
-// tile_done / gu_bn: the tile counters and the gate/up item width of the
-// single launch (SYNC != kNoSync).
+// sync / GU_BN: the sync words (see kNoSync) and the gate/up item width of
+// the single launch (SYNC != kNoSync).
 template <Elem EL, int WAVES, int BM, int SS, bool SWIGLU, int AD, int SYNC, int GU_BN = 0,
           bool WIDE = false>
 __device__ __forceinline__ void stream_item(
     const GemmArgs &p, const int item, uint8_t *lds,
-    typename StreamCfg<EL, WAVES, BM, SS, SWIGLU, WIDE>::SAs &sAs, int32_t *tile_done) {
+    typename StreamCfg<EL, WAVES, BM, SS, SWIGLU, WIDE>::SAs &sAs, int32_t *sync) {
   using C = StreamCfg<EL, WAVES, BM, SS, SWIGLU, WIDE>;
   constexpr int ICOLS = C::ICOLS;
   constexpr int NMAT = C::NMAT, BN = C::BN, MB = C::MB, NPR = C::NPR;
@@ -162,11 +165,12 @@ __device__ __forceinline__ void stream_item(
       // down GEMM's K is the gate/up GEMM's N) have counted themselves
       if (tid == 0) {
         const int need = K / GU_BN;
-        for (int poll = 0; poll < kTileWaitPolls; ++poll) {
-          if (__hip_atomic_load(tile_done + ti, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need)
-            break;
-          __builtin_amdgcn_s_sleep(2);
+        bool ready = false;
+        for (int poll = 0; poll < kTileWaitPolls && !ready; ++poll) {
+          ready = __hip_atomic_load(sync + 1 + ti, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need;
+          if (!ready) __builtin_amdgcn_s_sleep(2);
         }
+        if (!ready) __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
     }
@@ -488,7 +492,7 @@ __device__ __forceinline__ void stream_item(
       // coherence before the tile counter says so
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(tile_done + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_fetch_add(sync + 1 + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // the next item's first barrier orders these LDS reads before reuse
   }
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 // separate launches, so the results are bitwise the same.
 template <int SSG, int SSD, bool WIDE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void stream_ffn_kernel(
-    const GemmArgs gu, const GemmArgs dn, int32_t *tile_done) {
+    const GemmArgs gu, const GemmArgs dn, int32_t *sync) {
   using CG = StreamCfg<Elem::BF16, 8, 64, SSG, true>;
   using CD = StreamCfg<Elem::BF16, 8, 64, SSD, false, WIDE>;
   constexpr int kLds = CG::LDS > CD::LDS ? CG::LDS : CD::LDS;
@@ -541,10 +545,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item >= n_all) break;
     if (item < n_gu)
-      stream_item<Elem::BF16, 8, 64, SSG, true, 1, kSignal>(gu, item, lds, sAsG, tile_done);
+      stream_item<Elem::BF16, 8, 64, SSG, true, 1, kSignal>(gu, item, lds, sAsG, sync);
     else
       stream_item<Elem::BF16, 8, 64, SSD, false, 2, kWait, CG::BN, WIDE>(dn, item - n_gu, lds,
-                                                                           sAsD, tile_done);
+                                                                           sAsD, sync);
   }
 }
 
@@ -589,7 +593,7 @@ hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
 constexpr int kWideBelowItemsPerSlot = 32;
 
 template <int SSG, int SSD, bool WIDE>
-hipError_t launch_ffn(const GemmArgs &gu, const GemmArgs &dn, int32_t *tile_done, hipStream_t s,
+hipError_t launch_ffn(const GemmArgs &gu, const GemmArgs &dn, int32_t *sync, hipStream_t s,
                       int slots) {
   const int64_t items =
       static_cast<int64_t>(gu.tiles_ub) * ((gu.N > gu.Ns ? gu.N : gu.Ns) / 128 +
@@ -597,7 +601,7 @@ hipError_t launch_ffn(const GemmArgs &gu, const GemmArgs &dn, int32_t *tile_done
   int64_t grid = slots;
   if (items < grid) grid = items;
   if (grid <= 0) return hipSuccess;
-  stream_ffn_kernel<SSG, SSD, WIDE><<<static_cast<unsigned>(grid), 512, 0, s>>>(gu, dn, tile_done);
+  stream_ffn_kernel<SSG, SSD, WIDE><<<static_cast<unsigned>(grid), 512, 0, s>>>(gu, dn, sync);
   return hipGetLastError();
 }
 
@@ -636,7 +640,7 @@ bool stream_ffn_supported(int elem, int bm, int hidden, int inter, int shared_in
          shared_inter % 128 == 0;
 }
 
-hipError_t launch_ffn_stream(const GemmArgs &gu, const GemmArgs &dn, int32_t *tile_done,
+hipError_t launch_ffn_stream(const GemmArgs &gu, const GemmArgs &dn, int32_t *sync,
                              hipStream_t s) {
   if (!stream_ffn_supported(1, 64, gu.K, gu.N, gu.Ns) || gu.K != gu.Ks || dn.N != gu.K ||
       dn.K != gu.N || dn.Ks != gu.Ns || gu.tiles != dn.tiles || gu.num_tiles != dn.num_tiles)
@@ -649,10 +653,10 @@ hipError_t launch_ffn_stream(const GemmArgs &gu, const GemmArgs &dn, int32_t *ti
   // down: 512-byte stages where every K allows them
   const bool ss512 = dn.K % 256 == 0 && dn.Ks % 256 == 0;
   if (wide)
-    return ss512 ? launch_ffn<512, 512, true>(gu, dn, tile_done, s, slots)
-                 : launch_ffn<512, 256, true>(gu, dn, tile_done, s, slots);
-  return ss512 ? launch_ffn<512, 512, false>(gu, dn, tile_done, s, slots)
-               : launch_ffn<512, 256, false>(gu, dn, tile_done, s, slots);
+    return ss512 ? launch_ffn<512, 512, true>(gu, dn, sync, s, slots)
+                 : launch_ffn<512, 256, true>(gu, dn, sync, s, slots);
+  return ss512 ? launch_ffn<512, 512, false>(gu, dn, sync, s, slots)
+               : launch_ffn<512, 256, false>(gu, dn, sync, s, slots);
 }
 
 hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a,

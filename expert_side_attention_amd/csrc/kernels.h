@@ -117,11 +117,13 @@ hipError_t launch_gemm_stream(GemmKind kind, int elem, int bm, const GemmArgs &a
                               hipStream_t s);
 // Both weight-streaming GEMMs (gate/up, then down) of a bf16 forward with
 // 64-row tiles in one persistent launch.  gu and dn use the same tile list;
-// tile_done holds one counter per tile of that list, zeroed before the
-// launch (the dispatch kernel does it).  stream_ffn_supported tells whether
-// a layer's shapes allow it.
+// sync holds 1 + one int per tile of that list, zeroed before the launch
+// (the dispatch kernel does it): sync[0] ends as the number of down items
+// that gave up waiting for their tile (0 unless defective), sync[1 + t] is
+// tile t's counter.  stream_ffn_supported tells whether a layer's shapes
+// allow it.
 bool stream_ffn_supported(int elem, int bm, int hidden, int inter, int shared_inter);
-hipError_t launch_ffn_stream(const GemmArgs &gu, const GemmArgs &dn, int32_t *tile_done,
+hipError_t launch_ffn_stream(const GemmArgs &gu, const GemmArgs &dn, int32_t *sync,
                              hipStream_t s);
 // Compute-bound kernel (bf16, bm 256).
 hipError_t launch_gemm_prefill(GemmKind kind, const GemmArgs &a, hipStream_t s);
@@ -150,6 +152,7 @@ struct FusedArgs {
   int32_t *ids;
   float *w;
   int32_t *counts, *offsets, *perm, *slot_row, *num_tiles, *num_big;
+  int32_t *sync_timeouts;  // zeroed (the traced count of the GEMMs' single launch)
   uint8_t *z;
   void *out;
 };

@@ -154,7 +154,8 @@ class FfnLayer:
               "perm": torch.empty((T * k,), dtype=torch.int32, device=d),
               "slot_row": torch.empty((T, k), dtype=torch.int32, device=d),
               "logits": torch.empty((T, E), dtype=torch.float32, device=d),
-              "num_tiles": torch.empty((2,), dtype=torch.int32, device=d)}
+              "num_tiles": torch.empty((2,), dtype=torch.int32, device=d),
+              "sync_timeouts": torch.empty((1,), dtype=torch.int32, device=d)}
         if self.mode == "w8a8":
             R = T * k + self.num_shared * T
             Z = max(self.inter, self.shared_inter if self.num_shared else 0)

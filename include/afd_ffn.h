@@ -148,7 +148,14 @@ typedef struct {
  *                           shared expert s on token t), Z = max(I, I_s);
  *                           shared rows hold I_s valid columns
  *   num_tiles [2] int32     row tiles of the expert GEMMs: weight-streaming
- *                           tiles, then compute-bound 256-row tiles          */
+ *                           tiles, then compute-bound 256-row tiles
+ *   sync_timeouts [1] int32 down items of the single launch of both
+ *                           weight-streaming GEMMs (config split_gemms = 0)
+ *                           that stopped waiting for their row tile's z
+ *                           after a bound (about a quarter of a second):
+ *                           0 unless the library is defective, in which case
+ *                           the call's output is not valid; 0 for other
+ *                           launch structures                               */
 typedef struct {
   int32_t *topk_ids;
   float *topk_w;
@@ -162,6 +169,7 @@ typedef struct {
   uint8_t *z_q;
   float *z_s;
   int32_t *num_tiles;
+  int32_t *sync_timeouts;
 } afd_ffn_trace;
 
 /* Create a layer handle: validates cfg and w, allocates the per-handle

@@ -41,11 +41,12 @@ def test_struct_layout_matches_c_compiler(tmp_path):
 #include <stddef.h>
 #include "afd_ffn.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(afd_ffn_config),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(afd_ffn_config),
          sizeof(afd_ffn_weights), sizeof(afd_ffn_trace),
          offsetof(afd_ffn_config, max_tokens), offsetof(afd_ffn_weights, down_s),
          offsetof(afd_ffn_weights, sh_down_s), offsetof(afd_ffn_trace, x_s),
-         offsetof(afd_ffn_trace, num_tiles));
+         offsetof(afd_ffn_trace, num_tiles), offsetof(afd_ffn_config, split_gemms),
+         offsetof(afd_ffn_trace, sync_timeouts));
   return 0;
 }
 """)
@@ -57,7 +58,8 @@ int main(void) {
     want = [ctypes.sizeof(F.afd_ffn_config), ctypes.sizeof(F.afd_ffn_weights),
             ctypes.sizeof(F.afd_ffn_trace), F.afd_ffn_config.max_tokens.offset,
             F.afd_ffn_weights.down_s.offset, F.afd_ffn_weights.sh_down_s.offset,
-            F.afd_ffn_trace.x_s.offset, F.afd_ffn_trace.num_tiles.offset]
+            F.afd_ffn_trace.x_s.offset, F.afd_ffn_trace.num_tiles.offset,
+            F.afd_ffn_config.split_gemms.offset, F.afd_ffn_trace.sync_timeouts.offset]
     assert got == want
 
 

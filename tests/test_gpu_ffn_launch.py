@@ -52,6 +52,9 @@ def test_single_launch_equals_split_launches(shape):
     syn, one, split = _layers(shape, seed=31)
     print(f"[ffn] {shape}", flush=True)
     x = to_device(syn.hidden(), DEV, True)
+    _, tr = one.forward(x, trace=True)
+    torch.cuda.synchronize()
+    assert int(tr["sync_timeouts"][0]) == 0  # every down item found its tile complete
     one.profile_enable(["gate_up", "down", "ffn"])
     split.profile_enable(["gate_up", "down", "ffn"])
     a = one.forward(x).clone()

@@ -62,6 +62,8 @@ def check_full(name, microbatches=1, n_sample=12):
     torch.cuda.synchronize()
     out = np.concatenate([_np(o) for o in outs])
     trs = [{kk: v.cpu().numpy() for kk, v in tr.items()} for tr in trs]
+    # no down item of a single GEMM launch gave up waiting for its row tile
+    assert all(int(tr["sync_timeouts"][0]) == 0 for tr in trs)
     print(f"[fullsize] {name}: GPU done; oracle routing", flush=True)
 
     orc = O.OracleFFN(syn, threads=16)

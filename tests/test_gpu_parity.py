@@ -41,6 +41,8 @@ def check_layer(syn, x_store=None, threads=8, expect_exact_routing=False, single
     x = syn.hidden() if x_store is None else x_store
     print(f"[parity] {s} single_launch={single_launch}", flush=True)
     _, out, tr = run_gpu(syn, x, single_launch=single_launch)
+    # no down item of a single GEMM launch gave up waiting for its row tile
+    assert int(tr["sync_timeouts"][0]) == 0
     orc = O.OracleFFN(syn, threads=threads)
     ref = orc.forward(x)
     x64 = decode_store(x, s.mode)
