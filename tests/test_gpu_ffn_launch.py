@@ -103,3 +103,29 @@ def test_single_launch_batch_split_and_two_streams():
     assert torch.equal(torch.cat([o0, o1]).view(torch.int16), full.view(torch.int16))
     for layer in (one, split, sib):
         layer.close()
+
+
+@pytest.mark.parametrize("name", ["decode_h4096_e64", "dsv3_decode_t512"])
+def test_single_launch_full_size_alternating_inputs(name):
+    """At the benchmark sizes (every CU, all XCDs): one handle alternating
+    three different batches gives, every time, the bits of the separate
+    launches on the same batch.  A z row read before its gate/up items had
+    written it through, or a line of an earlier forward's z served from a
+    cache, would show up here as a difference."""
+    from afd_inputs import CONFIGS
+    from expert_side_attention_amd.workload import to_device
+    shape = CONFIGS[name]
+    syn, one, split = _layers(shape, seed=0)
+    print(f"[ffn] full size {name}", flush=True)
+    base = to_device(syn.hidden(), DEV, True)
+    xs = [base, base.flip(0).contiguous(), torch.roll(base, 7, dims=1).contiguous()]
+    refs = [split.forward(x).clone() for x in xs]
+    out = torch.empty_like(base)
+    for i in range(24):
+        j = i % 3
+        _, tr = one.forward(xs[j], out=out, trace=True)
+        torch.cuda.synchronize()
+        assert int(tr["sync_timeouts"][0]) == 0
+        assert torch.equal(out.view(torch.int16), refs[j].view(torch.int16)), (i, j)
+    one.close()
+    split.close()
