@@ -21,6 +21,9 @@
  *     experts                                 (experts are large matrix
  *                                              products, A/F 分离 page,
  *                                              "为什么要拆")
+ *     (bf16 batches of the decode regime run both GEMMs as one launch, in
+ *     which each down item waits for the gate/up items of its row tile;
+ *     the config's split_gemms = 1 asks for one launch per GEMM instead)
  *   deterministic weighted combine back into token order ("combine", A/F
  *                                              分离 page, "机制")
  *
